@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark one decode step of the paged KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the host block allocator reserves each sequence's slot (copy-on-write pairs
+where a shared block is written; done once, outside the timed region), then
+on the GPU copy_blocks on those pairs, reshape_and_cache of each sequence's
+new token, and paged_attention_decode over all cached tokens (main kernel,
+plus the log-sum-exp merge when a sequence spans several partitions).
+
+Timing: W warm-up steps, then K timed steps.  Before each step a 1 GiB
+buffer is written to evict the L2s and the Infinity Cache (outside the
+events).  Each step is bracketed by HIP events on the stream the kernels
+run on; the main attention kernel is bracketed by its own pair of events,
+recorded by the library right around its launch.
+
+Output: one JSON line (rank 0).  value = KV bytes read by attention per
+step / mean step time, in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+WORKLOADS = {
+    "tiny": "tiny paged decode: 4 seqs L={17,33,64,100}, 8/8 heads, d 64, Bs 16, fp32",
+    "7b": "Llama-2-7B-shaped decode: batch 64, 32/32 heads, d 128, bf16, Bs 16, L~U[512,2048]",
+    "70b": "70B-shaped GQA decode: batch 256, 64/8 heads, d 128, bf16, Bs 16, L~U[128,4096]",
+    "shared": "shared-prefix sampling: 64 seqs x (4000-token shared prompt + tail U[0,512]), "
+              "32/8 heads, d 128, bf16, Bs 16, CoW step",
+    "long": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 16",
+    "long32": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 32",
+}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def build_step(name, ps, device):
+    import workloads as W
+    from paged_kv_cache_305_amd.step import shared_prefix_step, step_from_case
+    if name == "shared":
+        plan = W.shared_plan()
+        tens = W.shared_tensors(plan, device=device)
+        step, rec = shared_prefix_step(plan, tens, partition_size=ps)
+        lens = rec["lens"].astype(np.int64)
+        return step, lens, dict(seed=plan.seed, cow_pairs=int(rec["pairs"].shape[0]),
+                                num_blocks=plan.num_blocks)
+    base = "long" if name == "long32" else name
+    kw = dict(block_size=32) if name == "long32" else {}
+    case = W.make_case(base, device=device, **kw)
+    step = step_from_case(case, partition_size=ps)
+    return step, case.context_lens.astype(np.int64), dict(seed=case.seed,
+                                                          num_blocks=case.num_blocks)
+
+
+def algorithmic_bytes(step, lens):
+    """Bytes the attention op must move: each KV head's tokens once (K and V),
+    q in, out back, the used table entries and the lengths."""
+    B, hq, d = step.query.shape
+    esz = step.query.element_size()
+    kv = int(lens.sum()) * step.num_kv_heads * d * 2 * esz
+    qo = B * hq * d * (esz + step.out.element_size())
+    tables = 4 * int(np.sum(-(-lens // step.block_size))) + 4 * B
+    return kv, kv + qo + tables
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_cache.hip"):
+        with open(os.path.join(ROOT, "paged_kv_cache_305_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, ps):
+    """HBM bytes per main-kernel launch from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_ps%d.json" % (workload, ps))
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(step, lens, max_seconds):
+    """The oracle, as it stands, on this host's cores, over a bounded sample."""
+    import oracle
+    import workloads as W
+    threads = max(1, min(16, os.cpu_count() or 1))
+    kc = W.host_array(step.key_cache)
+    vc = W.host_array(step.value_cache)
+    q = W.host_array(step.query)
+    tab = step.block_tables.cpu().numpy()
+    ln = step.context_lens.cpu().numpy()
+    B = q.shape[0]
+    # Grow the sample (a prefix of the batch) until it costs ~max_seconds.
+    n, spent, done_bytes, done_seqs = 1, 0.0, 0, 0
+    start = 0
+    while start < B and spent < max_seconds:
+        n = min(n, B - start)
+        t0 = time.perf_counter()
+        oracle.paged_attention(q[start:start + n], kc, vc, tab[start:start + n],
+                               ln[start:start + n], num_kv_heads=step.num_kv_heads,
+                               head_dim=step.head_dim, block_size=step.block_size,
+                               scale=step.scale, num_blocks=step.num_blocks, threads=threads)
+        spent += time.perf_counter() - t0
+        done_bytes += int(lens[start:start + n].sum()) * step.num_kv_heads * step.head_dim * 2 * \
+            step.query.element_size()
+        done_seqs += n
+        start += n
+        per_seq = spent / done_seqs
+        n = max(1, min(2 * n, int((max_seconds - spent) / per_seq)))
+    return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=threads,
+                kind="oracle", seconds=round(spent, 3),
+                tokens_per_s=round(done_seqs / spent, 3),
+                sample="first %d of %d sequences of the same step (fp64 gather + naive softmax "
+                       "attention, %d threads)" % (done_seqs, B, threads))
+
+
+def copy_calibration(device, steps):
+    """A plain 1 GiB device copy, for scaling the FETCH/WRITE counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    b = torch.empty_like(a)
+    for i in range(steps):
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy %d/%d done" % (i + 1, steps))
+    print(json.dumps({"copy_bytes": n, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_305_amd as pa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pa.load()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    if args.copy_calibration:
+        copy_calibration(device, max(1, args.steps))
+        return
+
+    log("building workload %s" % args.workload)
+    step, lens, info = build_step(args.workload, args.partition_size, device)
+    torch.cuda.synchronize()
+    kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    K, W_ = args.steps, args.warmup
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    s_ev, e_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
+    ms_ev, me_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
+
+    log("warmup %d steps" % W_)
+    for _ in range(W_):
+        if flush is not None:
+            flush.zero_()
+        step.run()
+    torch.cuda.synchronize()
+    log("timing %d steps" % K)
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush.zero_()
+        pa.set_timing_events(ms_ev[i], me_ev[i])
+        s_ev[i].record()
+        step.run()
+        e_ev[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pa.set_timing_events(None, None)
+    step_ms = [s.elapsed_time(e) for s, e in zip(s_ev, e_ev)]
+    main_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, me_ev)]
+    t_step = float(np.mean(step_ms)) / 1e3
+    t_main = float(np.mean(main_ms)) / 1e3
+    log("step %.1f us (median %.1f), main kernel %.1f us" % (
+        t_step * 1e6, float(np.median(step_ms)) * 1e3, t_main * 1e6))
+
+    B = int(step.query.shape[0])
+    gbs = kv_bytes / t_step / 1e9
+    achieved = attn_bytes / t_main / 1e9
+    kernel = "decode_mfma" if (step.query.dtype == torch.bfloat16 and
+                              step.query.shape[1] // step.num_kv_heads >= 2) else "decode_valu"
+    roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=counter_traffic(args.workload, args.partition_size),
+                algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2))
+    result = {
+        "metric": "paged decode attention KV GB/s (fraction of HBM peak) and tokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W_,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[step.query.dtype],
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block permutation)",
+        "config": {"workload": WORKLOADS[args.workload], "partition_size": args.partition_size,
+                   "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
+                   "flush_between_steps": flush is not None, **info},
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B / t_step, 1),
+        "kv_tokens_per_s": round(float(lens.sum()) / t_step, 1),
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(step, lens, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

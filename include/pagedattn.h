@@ -1,0 +1,232 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: paged decode attention for MI355X
+ * (gfx950) and the block management around it.
+ *
+ * The method (dmarx anthology note-023 "Method"; crackai.dev summary of Kwon
+ * et al., "How It Works"): each sequence's KV cache is cut into fixed-size
+ * blocks of block_size tokens, a per-sequence block table maps logical block
+ * index to physical block, and the attention kernel gathers K/V from those
+ * scattered physical blocks.  A block is taken only when a sequence's growth
+ * needs one and returned when the sequence ends; sequences with a common
+ * prefix point at the same blocks, and a shared block is duplicated only
+ * when one of its sharers writes to it.
+ *
+ * Conventions
+ *  - Every call returns pa_status; PA_OK is 0, errors are negative.  On an
+ *    error nothing is launched and no state changes; pa_last_error() gives a
+ *    message for the calling thread.  No exception crosses this boundary.
+ *  - Device pointers are caller-owned (for example PyTorch tensors),
+ *    contiguous, and 16-byte aligned.  The library never allocates or frees
+ *    device memory.
+ *  - Kernel calls are asynchronous on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream) and never synchronise.
+ *  - Cheap scalar checks always run.  With the environment variable
+ *    PA_VALIDATE=1 the kernel calls also copy their integer inputs to the
+ *    host (synchronously) and check every table entry, slot and pair.
+ *
+ * Pool layout (one layer; K and V in separate pools), x = 16 / element size:
+ *    key   pool [num_blocks][num_kv_heads][head_dim / x][block_size][x]
+ *    value pool [num_blocks][num_kv_heads][head_dim][block_size]
+ *  so every (block, KV head) chunk is block_size * head_dim contiguous
+ *  elements; keys keep 16-byte runs of one token's features, values keep
+ *  each feature's block_size tokens together.  A slot is
+ *  physical_block * block_size + offset_in_block.
+ *
+ * Allocator handles are library-owned host objects, not thread-safe, and
+ * destroyed by the caller.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG (-1)   /* bad pointer, size, range or alignment   */
+#define PA_ERR_UNSUPPORTED (-2)   /* valid but not built: head_dim, block_size */
+#define PA_ERR_OUT_OF_BLOCKS (-3) /* allocator pool exhausted                 */
+#define PA_ERR_UNKNOWN_SEQ (-4)   /* allocator: no such sequence id           */
+#define PA_ERR_HIP (-5)           /* a HIP runtime call failed                */
+
+typedef int32_t pa_dtype;
+#define PA_FP32 0
+#define PA_BF16 1
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char *pa_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t pa_version(void);
+
+/* ------------------------------------------------------------------------
+ * paged_attention_decode -- single-query attention of every sequence over
+ * its cached tokens, read through its block table rather than from one
+ * contiguous buffer (note-023 "Concepts", PagedAttention).  The result is plain softmax
+ * attention; paging changes where the bytes come from, not the attention
+ * computation (inferensys glossary "Paged Attention", fourth paragraph).
+ *
+ *  out            [num_seqs][num_q_heads][head_dim] in out_dtype (device, written)
+ *  query          [num_seqs][num_q_heads][head_dim] in kv_dtype (device)
+ *  key_cache      key pool, layout above, kv_dtype (device)
+ *  value_cache    value pool, layout above, kv_dtype (device)
+ *  block_tables   int32 [num_seqs][max_blocks_per_seq], row-major (device);
+ *                 entry j of row i is the physical block of tokens
+ *                 j*block_size .. (j+1)*block_size-1 of sequence i.  Entries
+ *                 at or past ceil(L_i / block_size) are never read.
+ *  context_lens   int32 [num_seqs] (device): L_i cached tokens of sequence i,
+ *                 0 <= L_i <= max_context_len.  L_i = 0 gives a zero row.
+ *  num_blocks     physical blocks in each pool (used by PA_VALIDATE checks).
+ *  Query head h attends with KV head h / (num_q_heads / num_kv_heads)
+ *  (grouped-query attention, inferensys glossary, GQA paragraph).
+ *  scale          multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ *  max_context_len  host upper bound of every L_i; sizes the launch without
+ *                 a device read.  Must be <= max_blocks_per_seq * block_size.
+ *  partition_size 0: one pass per (sequence, head).  Otherwise a positive
+ *                 multiple of block_size: each sequence's context is split
+ *                 into ceil(L_i / partition_size) partitions computed
+ *                 independently and merged exactly by a log-sum-exp reduce.
+ *  workspace      device scratch of at least
+ *                 pa_paged_attention_workspace_bytes(...) bytes when that is
+ *                 nonzero (caller-owned, contents need not be initialised).
+ *  Supported: head_dim in {64, 128}, block_size in {16, 32},
+ *  kv_dtype/out_dtype in {PA_FP32, PA_BF16}; anything else returns
+ *  PA_ERR_UNSUPPORTED.  bf16 outputs are rounded to nearest even.
+ * ---------------------------------------------------------------------- */
+pa_status pa_paged_attention_decode(void *out, const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t max_context_len, float scale,
+                                    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Tracing hook: while set, every pa_paged_attention_decode call records
+ * hipEvent_t `before_main` just before its main attention kernel and
+ * `after_main` just after it, on the call's stream (the log-sum-exp merge
+ * kernel, when launched, comes after `after_main`).  Pass NULL, NULL to
+ * stop.  The events are caller-owned; the setting is process-wide and not
+ * thread-safe.  Used to time the main kernel alone. */
+pa_status pa_set_timing_events(void *before_main, void *after_main);
+
+/* Bytes of workspace pa_paged_attention_decode needs for these sizes; 0 when
+ * no sequence can have more than one partition.  Returns 0 for invalid
+ * arguments too (the decode call then reports them). */
+size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t head_dim, int32_t max_context_len,
+                                          int32_t partition_size);
+
+/* ------------------------------------------------------------------------
+ * reshape_and_cache -- write each new token's K/V into its slot of the
+ * pools: blocks are taken as a sequence grows, one token at a time
+ * (note-023 "Method"; crackai.dev "How It Works", KV cache pages).  Bit
+ * copy, no conversion.
+ *
+ *  key, value     [num_tokens][num_kv_heads][head_dim] in dtype (device)
+ *  key_cache, value_cache  pools, layout above (device, written)
+ *  slot_mapping   int64 [num_tokens] (device): block * block_size + offset;
+ *                 a negative slot skips the token.  Slots must be
+ *                 < num_blocks * block_size and distinct (a repeated slot is
+ *                 a caller error; PA_VALIDATE=1 rejects it).
+ * ---------------------------------------------------------------------- */
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * copy_blocks -- the copy of copy-on-write: a sequence writing into a shared
+ * block first gets a private duplicate (note-023 "Concepts", copy-on-write;
+ * inferensys glossary, second paragraph).  Copies whole blocks, K and V,
+ * every head and every slot.
+ *
+ *  block_mapping  int64 [num_pairs][2] (device): (src, dst) physical blocks.
+ *                 A src may repeat; dsts must be distinct and not among the
+ *                 srcs, so the result does not depend on order (PA_VALIDATE=1
+ *                 rejects violations).  num_pairs = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int64_t *block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Block allocator (host).  Free list, reference counts and copy-on-write
+ * over a pool of num_blocks physical blocks (note-023 "Method" and
+ * "Concepts"; inferensys glossary, first and second paragraphs; crackai.dev
+ * "How It Works").  Policy where the pages leave it open:
+ *  - the free list is a LIFO stack;
+ *  - a finished sequence's blocks are pushed from its last logical block to
+ *    its first, so its first block is the next one handed out (the
+ *    skillsintelligence glossary's worked example: a finished request's
+ *    blocks go to a newly arriving request in the following step);
+ *  - a copy happens only when appending into a partially filled last block
+ *    whose refcount is above 1; a full shared block is never copied;
+ *  - every call is all-or-nothing: on an error the state is unchanged.
+ * Sequence ids are arbitrary int64 values chosen by the caller.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_allocator pa_allocator;
+
+/* New allocator over num_blocks blocks of block_size tokens.  With
+ * initial_free_order == NULL the first blocks handed out are 0, 1, 2, ...;
+ * otherwise initial_free_order[0..num_blocks-1] (a permutation of
+ * 0..num_blocks-1, copied) gives the order of the first hand-outs.  Returns
+ * NULL on invalid arguments (see pa_last_error). */
+pa_allocator *pa_allocator_create(int64_t num_blocks, int32_t block_size,
+                                  const int32_t *initial_free_order);
+void pa_allocator_destroy(pa_allocator *a);
+int64_t pa_allocator_num_free(const pa_allocator *a);
+int32_t pa_allocator_block_size(const pa_allocator *a);
+
+/* A sequence holding num_tokens prompt tokens in ceil(num_tokens/block_size)
+ * fresh blocks (refcount 1).  PA_ERR_INVALID_ARG if seq_id exists or
+ * num_tokens < 0; PA_ERR_OUT_OF_BLOCKS if the pool cannot hold it. */
+pa_status pa_seq_create(pa_allocator *a, int64_t seq_id, int64_t num_tokens);
+
+/* child shares every block of parent (each refcount + 1) and its length:
+ * parallel sampling and beam search share the prompt's blocks (inferensys
+ * glossary, second paragraph; crackai.dev, copy-on-write sharing). */
+pa_status pa_seq_fork(pa_allocator *a, int64_t parent_id, int64_t child_id);
+
+/* Reserve position L (the sequence then holds L + 1 tokens) and return its
+ * slot.  If L % block_size == 0 a fresh block is appended.  Otherwise, if
+ * the last block is shared (refcount > 1), a fresh block dst replaces it in
+ * this sequence's table, the old block src loses one reference, and
+ * (*cow_src, *cow_dst) = (src, dst); else the write goes in place and both
+ * are -1.  The caller must run pa_copy_blocks on every returned pair before
+ * pa_reshape_and_cache writes the slot. */
+pa_status pa_seq_append_slot(pa_allocator *a, int64_t seq_id, int64_t *slot, int64_t *cow_src,
+                             int64_t *cow_dst);
+
+/* Release a finished sequence: each block loses one reference and blocks
+ * reaching zero return to the free list (last logical block first). */
+pa_status pa_seq_free(pa_allocator *a, int64_t seq_id);
+
+/* Copy the sequence's physical blocks into out[0..capacity); *n_out gets the
+ * count.  PA_ERR_INVALID_ARG if capacity is too small (nothing written). */
+pa_status pa_seq_block_table(const pa_allocator *a, int64_t seq_id, int32_t *out,
+                             int32_t capacity, int32_t *n_out);
+
+/* Tokens held by the sequence, or -1 if unknown. */
+int64_t pa_seq_len(const pa_allocator *a, int64_t seq_id);
+
+/* References to a physical block (0 = free), or -1 if out of range. */
+int32_t pa_block_refcount(const pa_allocator *a, int32_t block);
+
+/* Pack the tables and lengths of n sequences for upload: out_tables is a
+ * host int32 [n][max_blocks] filled with each table, padded with pad;
+ * out_lens a host int32 [n].  PA_ERR_INVALID_ARG if a table is longer than
+ * max_blocks or a length exceeds INT32_MAX. */
+pa_status pa_build_block_tables(const pa_allocator *a, const int64_t *seq_ids, int32_t n,
+                                int32_t max_blocks, int32_t pad, int32_t *out_tables,
+                                int32_t *out_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

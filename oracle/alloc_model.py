@@ -3,8 +3,9 @@
 Follows the memory-management operations the pages state:
   * fixed-size blocks, a per-sequence table of logical -> physical block
     (dmarx note-023, Method; crackai.dev "How It Works", block table);
-  * blocks allocated on demand as a sequence grows, never reserved for a
-    maximum length (note-023 Method; crackai.dev, on-demand allocation);
+  * a block is taken only when a sequence's growth needs one, never
+    reserved up front for a maximum length (note-023 Method; crackai.dev,
+    on-demand allocation);
   * blocks freed when a sequence finishes and reused right away
     (note-023 Method; skillsintelligence glossary, worked example);
   * physical blocks shared by reference between sequences with a common

@@ -8,8 +8,8 @@
  *
  * What it computes (all from the method as the pages state it):
  *
- *  - paged attention: "PagedAttention, and vLLM around it" (dmarx note-023,
- *    Method; Concepts "PagedAttention") -- the kernel reads each sequence's
+ *  - paged attention (dmarx note-023, Method; Concepts "PagedAttention"):
+ *    the kernel reads each sequence's
  *    K/V through a per-sequence block table that maps logical block index to
  *    physical block, and the result is plain softmax attention, the gain
  *    coming from memory management alone and not from changing the attention
@@ -20,13 +20,14 @@
  *    query head h reads KV head h / (Hq / Hkv).
  *
  *  - reshape_and_cache: the new token's K/V are written into the slot the
- *    block table gives it ("allocate blocks on demand as a sequence grows",
- *    note-023 Method; crackai.dev "How It Works", KV cache pages).  A slot is
- *    block * Bs + offset; a negative slot is skipped.  Bit copy.
+ *    block table gives it -- a block is taken only when a sequence's
+ *    growth needs one (note-023 Method; crackai.dev "How It Works", KV cache
+ *    pages).  A slot is block * Bs + offset; a negative slot is skipped.
+ *    Bit copy.
  *
- *  - copy_blocks: copy-on-write gives a writer "its own copy" of a shared
- *    block (note-023 Concepts "Copy-on-write"; inferensys, second
- *    paragraph).  The whole block is copied, K and V, every head and slot.
+ *  - copy_blocks: under copy-on-write a sequence that writes to a shared
+ *    block is given a private duplicate of it (note-023 Concepts
+ *    "Copy-on-write"; inferensys, second paragraph).  The whole block is copied, K and V, every head and slot.
  *    All sources are read before any destination is written.
  *
  * Pool layout (the library's, stated here so the oracle can address it):

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) paged decode attention.
+
+The data-parallel hot path of PagedAttention as a C-ABI library
+(``libpagedattn.so``, declared in ``include/pagedattn.h``) with this thin
+Python binding:
+
+  * ``paged_attention_decode`` -- single-query attention read through
+    per-sequence block tables (HIP kernels; MFMA for grouped-query heads);
+  * ``reshape_and_cache`` -- write new tokens' K/V into their slots;
+  * ``copy_blocks`` -- the copy of copy-on-write;
+  * ``BlockAllocator`` -- host free list, refcounts and copy-on-write.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARG, PA_ERR_OUT_OF_BLOCKS,
+    PA_ERR_UNKNOWN_SEQ, PA_ERR_UNSUPPORTED, PA_FP32, PA_OK, BlockAllocator, PagedAttnError,
+    allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
+    paged_attention_workspace_bytes, reshape_and_cache, set_timing_events, value_cache_shape)

@@ -1,0 +1,348 @@
+"""ctypes binding of libpagedattn.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels or its host
+allocator.  PyTorch provides device memory (tensors) and streams; this module
+checks tensor placement/dtype/contiguity, derives sizes, and passes
+``data_ptr()`` values and the current HIP stream across the C ABI.  If the
+library is missing it is built once from source; if it cannot be loaded,
+every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_OUT_OF_BLOCKS = -3
+PA_ERR_UNKNOWN_SEQ = -4
+PA_ERR_HIP = -5
+PA_FP32 = 0
+PA_BF16 = 1
+
+# Every symbol include/pagedattn.h declares.
+EXPORTS = (
+    "pa_last_error", "pa_version",
+    "pa_paged_attention_decode", "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
+    "pa_reshape_and_cache", "pa_copy_blocks",
+    "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free",
+    "pa_allocator_block_size", "pa_seq_create", "pa_seq_fork", "pa_seq_append_slot",
+    "pa_seq_free", "pa_seq_block_table", "pa_seq_len", "pa_block_refcount",
+    "pa_build_block_tables",
+)
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(lib):
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    p_i32, p_i64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "pa_last_error": (ctypes.c_char_p, []),
+        "pa_version": (i32, []),
+        "pa_paged_attention_decode": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i64, i32, f32, i32, i32, i32, vp, sz, vp]),
+        "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "pa_set_timing_events": (i32, [vp, vp]),
+        "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
+        "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
+        "pa_allocator_create": (vp, [i64, i32, vp]),
+        "pa_allocator_destroy": (None, [vp]),
+        "pa_allocator_num_free": (i64, [vp]),
+        "pa_allocator_block_size": (i32, [vp]),
+        "pa_seq_create": (i32, [vp, i64, i64]),
+        "pa_seq_fork": (i32, [vp, i64, i64]),
+        "pa_seq_append_slot": (i32, [vp, i64, p_i64, p_i64, p_i64]),
+        "pa_seq_free": (i32, [vp, i64]),
+        "pa_seq_block_table": (i32, [vp, i64, vp, i32, p_i32]),
+        "pa_seq_len": (i64, [vp, i64]),
+        "pa_block_refcount": (i32, [vp, i32]),
+        "pa_build_block_tables": (i32, [vp, vp, i32, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load():
+    """Load (building once if absent) libpagedattn.so; returns the ctypes handle."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch first: its HIP runtime is then the one the library binds to
+    # (both carry the same SONAME), so torch's stream handles are valid here.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    _declare(lib)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError("two HIP runtimes are mapped (%s); load torch before this library"
+                           % ", ".join(sorted(runtimes)))
+    _lib = lib
+    return lib
+
+
+def _err(status: int) -> PagedAttnError:
+    msg = load().pa_last_error()
+    return PagedAttnError(status, msg.decode() if msg else "")
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise _err(status)
+
+
+# ---- tensors -----------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_FP32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev(t, name, device=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    return t
+
+
+def _stream(device, stream) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return int(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def key_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype):
+    """[num_blocks, Hkv, d / x, block_size, x], x = 16 bytes / element size."""
+    x = 16 // _torch().empty((), dtype=dtype).element_size()
+    return (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+
+
+def value_cache_shape(num_blocks, num_kv_heads, head_dim, block_size):
+    """[num_blocks, Hkv, d, block_size]."""
+    return (num_blocks, num_kv_heads, head_dim, block_size)
+
+
+def allocate_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device="cuda"):
+    """Empty key and value pools in the library's layout."""
+    torch = _torch()
+    k = torch.empty(key_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype),
+                    dtype=dtype, device=device)
+    v = torch.empty(value_cache_shape(num_blocks, num_kv_heads, head_dim, block_size),
+                    dtype=dtype, device=device)
+    return k, v
+
+
+def set_timing_events(before_main=None, after_main=None):
+    """Record these torch.cuda.Events around the main attention kernel of every
+    later decode call (None, None stops)."""
+    h = lambda e: None if e is None else int(e.cuda_event)
+    _check(load().pa_set_timing_events(h(before_main), h(after_main)))
+
+
+def paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                    partition_size) -> int:
+    return int(load().pa_paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                         max_context_len, partition_size))
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, *,
+                           num_kv_heads: int, block_size: int, max_context_len: int,
+                           scale: float, partition_size: int = 0, workspace=None,
+                           num_blocks: Optional[int] = None, stream=None):
+    """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables."""
+    lib = load()
+    dev = query.device
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _dev(t, n, dev)
+    torch = _torch()
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_q_heads, head_dim]")
+    B, hq, d = query.shape
+    if tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must have the query's shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise TypeError("query and pools must share a dtype")
+    nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    chunk = num_kv_heads * d * block_size
+    if key_cache.numel() < nb * chunk or value_cache.numel() < nb * chunk:
+        raise ValueError("pools hold fewer than num_blocks blocks")
+    need = paged_attention_workspace_bytes(B, hq, d, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (
+        _dev(workspace, "workspace", dev).data_ptr(), workspace.numel() * workspace.element_size())
+    _check(lib.pa_paged_attention_decode(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
+        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
+        _dtype_code(query), _dtype_code(out), ws_ptr, ws_bytes, _stream(dev, stream)))
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, block_size: int,
+                      num_blocks: Optional[int] = None, stream=None):
+    """Write key/value [T, Hkv, d] into their slots of the pools (bit copy)."""
+    lib = load()
+    dev = key.device
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
+        _dev(t, n, dev)
+    if slot_mapping.dtype != _torch().int64:
+        raise TypeError("slot_mapping must be int64")
+    if key.dim() != 3 or key.shape != value.shape:
+        raise ValueError("key and value must be [num_tokens, num_kv_heads, head_dim]")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("key, value and pools must share a dtype")
+    T, hkv, d = key.shape
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _check(lib.pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, hkv, d, block_size, nb, _dtype_code(key),
+        _stream(dev, stream)))
+
+
+def copy_blocks(key_cache, value_cache, block_mapping, *, num_kv_heads: int, head_dim: int,
+                block_size: int, num_blocks: Optional[int] = None, stream=None):
+    """Copy whole blocks src -> dst in both pools; block_mapping is int64 [n, 2]."""
+    lib = load()
+    dev = key_cache.device
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_mapping, "block_mapping")):
+        _dev(t, n, dev)
+    if block_mapping.dtype != _torch().int64:
+        raise TypeError("block_mapping must be int64")
+    if block_mapping.numel() % 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _check(lib.pa_copy_blocks(
+        key_cache.data_ptr(), value_cache.data_ptr(), block_mapping.data_ptr(),
+        block_mapping.numel() // 2, num_kv_heads, head_dim, block_size, nb,
+        _dtype_code(key_cache), _stream(dev, stream)))
+
+
+# ---- allocator -----------------------------------------------------------------
+
+class BlockAllocator:
+    """Host block allocator (free list, refcounts, copy-on-write) owned by the library."""
+
+    def __init__(self, num_blocks: int, block_size: int,
+                 initial_free_order: Optional[Sequence[int]] = None):
+        lib = load()
+        self._lib = lib
+        order = None
+        ptr = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(np.asarray(initial_free_order, dtype=np.int32))
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_free_order must hold num_blocks entries")
+            ptr = order.ctypes.data
+        h = lib.pa_allocator_create(int(num_blocks), int(block_size), ptr)
+        if not h:
+            raise _err(PA_ERR_INVALID_ARG)
+        self._h = ctypes.c_void_p(h)
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_allocator_num_free(self._h))
+
+    def create(self, seq_id: int, num_tokens: int):
+        _check(self._lib.pa_seq_create(self._h, int(seq_id), int(num_tokens)))
+
+    def fork(self, parent_id: int, child_id: int):
+        _check(self._lib.pa_seq_fork(self._h, int(parent_id), int(child_id)))
+
+    def append_slot(self, seq_id: int):
+        """Returns (slot, cow_src, cow_dst); the pair is (-1, -1) when nothing is copied."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(self._lib.pa_seq_append_slot(self._h, int(seq_id), ctypes.byref(slot),
+                                            ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def free(self, seq_id: int):
+        _check(self._lib.pa_seq_free(self._h, int(seq_id)))
+
+    def seq_len(self, seq_id: int) -> int:
+        return int(self._lib.pa_seq_len(self._h, int(seq_id)))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_block_refcount(self._h, int(block)))
+
+    def block_table(self, seq_id: int) -> list:
+        n = ctypes.c_int32()
+        L = self.seq_len(seq_id)
+        cap = max(1, -(-max(L, 0) // self.block_size))
+        buf = np.zeros(cap, dtype=np.int32)
+        _check(self._lib.pa_seq_block_table(self._h, int(seq_id), buf.ctypes.data, cap,
+                                            ctypes.byref(n)))
+        return buf[:n.value].tolist()
+
+    def build_block_tables(self, seq_ids, max_blocks: int, pad: int = 0):
+        """Host int32 tables [n, max_blocks] (padded) and lengths [n] for upload."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = int(ids.shape[0])
+        tabs = np.empty((n, max_blocks), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        _check(self._lib.pa_build_block_tables(self._h, ids.ctypes.data, n, int(max_blocks),
+                                               int(pad), tabs.ctypes.data, lens.ctypes.data))
+        return tabs, lens

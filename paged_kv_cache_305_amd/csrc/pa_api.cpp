@@ -1,0 +1,266 @@
+// C ABI of the kernel calls: argument checks, workspace layout, optional deep
+// validation (PA_VALIDATE=1), then the launches.  Nothing here synchronises
+// unless PA_VALIDATE=1 asks for the integer inputs on the host.
+#include <hip/hip_runtime_api.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <unordered_set>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(pa_dtype t) { return t == PA_FP32 ? 4 : (t == PA_BF16 ? 2 : 0); }
+
+bool deep_validation() {
+  const char *v = getenv("PA_VALIDATE");
+  return v && v[0] == '1';
+}
+
+pa_status hip_fail(const char *what, int err) {
+  return pa_fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+template <typename T>
+pa_status to_host(std::vector<T> &dst, const T *src, size_t n, void *stream) {
+  dst.resize(n);
+  if (n == 0) return PA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e == hipSuccess ? PA_OK : hip_fail("PA_VALIDATE copy", (int)e);
+}
+
+void *g_ev_before_main = nullptr;
+void *g_ev_after_main = nullptr;
+
+int32_t partitions_for(int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0) return 1;
+  const int32_t n = (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  return n > 0 ? n : 1;
+}
+
+}  // namespace
+
+namespace pa {
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t num_partitions) {
+  WorkspaceLayout w{0, 0, 0, 0};
+  if (num_partitions <= 1 || num_seqs <= 0 || num_q_heads <= 0) return w;
+  const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.max_off = 0;
+  w.sum_off = up(rows * sizeof(float));
+  w.acc_off = w.sum_off + up(rows * sizeof(float));
+  w.total = w.acc_off + up(rows * (size_t)head_dim * sizeof(float));
+  return w;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_set_timing_events(void *before_main, void *after_main) {
+  pa_clear_error();
+  if ((before_main == nullptr) != (after_main == nullptr))
+    return pa_fail(PA_ERR_INVALID_ARG, "pa_set_timing_events: set both events or neither");
+  g_ev_before_main = before_main;
+  g_ev_after_main = after_main;
+  return PA_OK;
+}
+
+size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t head_dim, int32_t max_context_len,
+                                          int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim,
+                              partitions_for(max_context_len, partition_size))
+      .total;
+}
+
+pa_status pa_paged_attention_decode(void *out, const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t max_context_len, float scale,
+                                    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_paged_attention_decode";
+  if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return pa_fail(PA_ERR_INVALID_ARG,
+                   "%s: num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                   num_q_heads, num_kv_heads);
+  if (elem_bytes(kv_dtype) == 0 || elem_bytes(out_dtype) == 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtypes must be PA_FP32 or PA_BF16", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, head_dim);
+  if (block_size != 16 && block_size != 32)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32)", fn, block_size);
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq and num_blocks must be positive",
+                   fn);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return pa_fail(PA_ERR_INVALID_ARG,
+                   "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]",
+                   fn, max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+    return pa_fail(PA_ERR_INVALID_ARG,
+                   "%s: partition_size %d must be 0 or a positive multiple of block_size %d", fn,
+                   partition_size, block_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: out, query and pools must be 16-byte aligned", fn);
+
+  const int32_t parts = partitions_for(max_context_len, partition_size);
+  const pa::WorkspaceLayout ws = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu", fn,
+                     ws.total, workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  }
+
+  if (deep_validation()) {
+    std::vector<int32_t> lens, tabs;
+    pa_status s = to_host(lens, context_lens, (size_t)num_seqs, stream);
+    if (s == PA_OK)
+      s = to_host(tabs, block_tables, (size_t)num_seqs * max_blocks_per_seq, stream);
+    if (s != PA_OK) return s;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      if (lens[i] < 0 || lens[i] > max_context_len)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: context_lens[%d] = %d outside [0, %d]", fn, i,
+                       lens[i], max_context_len);
+      const int32_t used = (lens[i] + block_size - 1) / block_size;
+      for (int32_t j = 0; j < used; ++j) {
+        const int32_t b = tabs[(size_t)i * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: block_tables[%d][%d] = %d outside [0, %lld)",
+                         fn, i, j, b, (long long)num_blocks);
+      }
+    }
+  }
+
+  pa::DecodeArgs a;
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.partition_size = partition_size;
+  a.num_partitions = parts;
+  a.kv_dtype = kv_dtype;
+  a.out_dtype = out_dtype;
+  char *wsb = static_cast<char *>(workspace);
+  a.ws_max = ws.total ? reinterpret_cast<float *>(wsb + ws.max_off) : nullptr;
+  a.ws_sum = ws.total ? reinterpret_cast<float *>(wsb + ws.sum_off) : nullptr;
+  a.ws_acc = ws.total ? reinterpret_cast<float *>(wsb + ws.acc_off) : nullptr;
+  a.ev_before_main = g_ev_before_main;
+  a.ev_after_main = g_ev_after_main;
+  const int e = pa::launch_decode(a, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, pa_dtype dtype, void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_reshape_and_cache";
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_FP32 or PA_BF16", fn);
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: sizes must be positive (num_tokens >= 0)", fn);
+  if ((head_dim * esz) % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: head_dim * element size must be a multiple of 16",
+                   fn);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: key, value and pools must be 16-byte aligned", fn);
+  if (deep_validation()) {
+    std::vector<int64_t> slots;
+    pa_status s = to_host(slots, slot_mapping, (size_t)num_tokens, stream);
+    if (s != PA_OK) return s;
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (slots[i] < 0) continue;
+      if (slots[i] >= num_blocks * block_size)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: slot_mapping[%d] = %lld >= %lld", fn, i,
+                       (long long)slots[i], (long long)(num_blocks * block_size));
+      if (!seen.insert(slots[i]).second)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: slot %lld repeats", fn, (long long)slots[i]);
+    }
+  }
+  const int e = pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                                             num_tokens, num_kv_heads, head_dim, block_size,
+                                             num_blocks, esz, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int64_t *block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_copy_blocks";
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_FP32 or PA_BF16", fn);
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: sizes must be positive (num_pairs >= 0)", fn);
+  const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * esz;
+  if (block_bytes % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block bytes must be a multiple of 16", fn);
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned16(key_cache) || !aligned16(value_cache))
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: pools must be 16-byte aligned", fn);
+  if (deep_validation()) {
+    std::vector<int64_t> m;
+    pa_status s = to_host(m, block_mapping, (size_t)num_pairs * 2, stream);
+    if (s != PA_OK) return s;
+    std::unordered_set<int64_t> srcs, dsts;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      for (int k = 0; k < 2; ++k)
+        if (m[2 * i + k] < 0 || m[2 * i + k] >= num_blocks)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: block_mapping[%d][%d] = %lld outside [0, %lld)",
+                         fn, i, k, (long long)m[2 * i + k], (long long)num_blocks);
+      srcs.insert(m[2 * i]);
+      if (!dsts.insert(m[2 * i + 1]).second)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: destination %lld repeats", fn,
+                       (long long)m[2 * i + 1]);
+    }
+    for (int64_t d : dsts)
+      if (srcs.count(d))
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: block %lld is both a source and a destination",
+                       fn, (long long)d);
+  }
+  const int e = pa::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
+                                       block_bytes, num_blocks, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Companion kernels of the paged KV cache for gfx950.
+//
+//  * reshape_and_cache: each new token's K/V go into the slot its block table
+//    gives it; a block is taken only when a sequence's growth needs one (dmarx
+//    note-023, "Method"; crackai.dev, "How It Works").  A slot is
+//    block * block_size + offset; negative slots are skipped.
+//  * copy_blocks: the copy half of copy-on-write, giving a writer its own
+//    copy of a shared block (note-023, "Concepts"; inferensys glossary,
+//    second paragraph).  Whole blocks: K and V, all heads, all slots.
+//
+// Both are bit copies.  Pool layout, x = 16 / element size:
+//   key   [num_blocks][Hkv][d / x][block_size][x]
+//   value [num_blocks][Hkv][d][block_size]
+// Indices read from device memory (slots, pairs) are range-checked before
+// use; out-of-range entries are skipped so a bad input can never fault.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread per (token, KV head, 16-byte feature chunk).  The key chunk is
+// one 16-byte store (keys keep x features of a token together); the value
+// chunk scatters to x rows of the [d][block_size] value slab.
+template <int ESZ>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const char *__restrict__ key, const char *__restrict__ value, char *__restrict__ key_cache,
+    char *__restrict__ value_cache, const int64_t *__restrict__ slots, int num_tokens,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks) {
+  constexpr int X = 16 / ESZ;
+  const int chunks = head_dim / X;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks;
+  if (gid >= total) return;
+  const int c = (int)(gid % chunks);
+  const int h = (int)((gid / chunks) % num_kv_heads);
+  const int64_t tok = gid / ((int64_t)chunks * num_kv_heads);
+  const int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_blocks * block_size) return;
+  const int64_t b = slot / block_size;
+  const int o = (int)(slot % block_size);
+  const int64_t src = ((tok * num_kv_heads + h) * head_dim + (int64_t)c * X) * ESZ;
+  const int64_t head_base = (b * num_kv_heads + h) * (int64_t)head_dim * block_size;
+  const u32x4 kv = *reinterpret_cast<const u32x4 *>(key + src);
+  *reinterpret_cast<u32x4 *>(key_cache + (head_base + ((int64_t)c * block_size + o) * X) * ESZ) =
+      kv;
+  const u32x4 vv = *reinterpret_cast<const u32x4 *>(value + src);
+  char *vdst = value_cache + (head_base + (int64_t)c * X * block_size + o) * ESZ;
+#pragma unroll
+  for (int e = 0; e < X; ++e) {
+    if (ESZ == 4) {
+      *reinterpret_cast<unsigned *>(vdst + (int64_t)e * block_size * ESZ) = vv[e];
+    } else {
+      const unsigned w = vv[e >> 1];
+      *reinterpret_cast<uint16_t *>(vdst + (int64_t)e * block_size * ESZ) =
+          (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+  }
+}
+
+// Grid: x = 16-byte pieces of a block, y = pair, z = pool (0 key, 1 value).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char *__restrict__ key_cache,
+                                                          char *__restrict__ value_cache,
+                                                          const int64_t *__restrict__ pairs,
+                                                          int64_t block_bytes,
+                                                          int64_t num_blocks) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.y];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.y + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  char *pool = blockIdx.z == 0 ? key_cache : value_cache;
+  const u32x4 *s = reinterpret_cast<const u32x4 *>(pool + src * block_bytes);
+  u32x4 *d = reinterpret_cast<u32x4 *>(pool + dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    d[i] = s[i];
+}
+
+}  // namespace
+
+int launch_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                             void *value_cache, const int64_t *slots, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, int32_t elem_bytes, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim * elem_bytes / 16);
+  if (threads == 0) return (int)hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+  const char *k = static_cast<const char *>(key);
+  const char *v = static_cast<const char *>(value);
+  char *kc = static_cast<char *>(key_cache);
+  char *vc = static_cast<char *>(value_cache);
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, k,
+                       v, kc, vc, slots, num_tokens, num_kv_heads, head_dim, block_size,
+                       num_blocks);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, k,
+                       v, kc, vc, slots, num_tokens, num_kv_heads, head_dim, block_size,
+                       num_blocks);
+  return (int)hipGetLastError();
+}
+
+int launch_copy_blocks(void *key_cache, void *value_cache, const int64_t *pairs,
+                       int32_t num_pairs, int64_t block_bytes, int64_t num_blocks, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t pieces = block_bytes / 16;
+  const int64_t gx64 = (pieces + 255) / 256;
+  const unsigned gx = (unsigned)(gx64 < 64 ? gx64 : 64);
+  // grid.y is limited to 65535: launch the pairs in chunks.
+  for (int32_t first = 0; first < num_pairs; first += 65535) {
+    const int32_t n = num_pairs - first < 65535 ? num_pairs - first : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)n, 2), dim3(256), 0, st,
+                       static_cast<char *>(key_cache), static_cast<char *>(value_cache),
+                       pairs + 2 * (int64_t)first, block_bytes, num_blocks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return (int)hipSuccess;
+}
+
+}  // namespace pa

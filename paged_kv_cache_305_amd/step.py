@@ -1,0 +1,145 @@
+"""One decode step of a paged KV cache, as a serving loop would run it.
+
+Host: the block allocator reserves each sequence's next slot, allocating a
+block at a block boundary and returning a (src, dst) copy pair when the
+last block is shared (copy-on-write).  Device, in stream order: copy_blocks
+on the pairs, reshape_and_cache of the new tokens into their slots, then
+paged_attention_decode over every sequence's cached tokens.
+
+The host part runs once when the step is built; ``run()`` only launches the
+three kernels, so it can be repeated (same pairs, same slots, same reads)
+for timing.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import _binding as B
+
+
+@dataclass
+class DecodeStep:
+    query: object            # [B, Hq, d]
+    key_cache: object
+    value_cache: object
+    new_key: object          # [B, Hkv, d]
+    new_value: object
+    slot_mapping: object     # int64 [B]
+    cow_pairs: object        # int64 [n, 2] (n may be 0)
+    block_tables: object     # int32 [B, max_blocks]
+    context_lens: object     # int32 [B]
+    out: object              # [B, Hq, d]
+    workspace: Optional[object]
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_context_len: int
+    scale: float
+    partition_size: int
+
+    @property
+    def num_pairs(self) -> int:
+        return int(self.cow_pairs.shape[0])
+
+    def copy(self, stream=None):
+        if self.num_pairs:
+            B.copy_blocks(self.key_cache, self.value_cache, self.cow_pairs,
+                          num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
+                          block_size=self.block_size, num_blocks=self.num_blocks, stream=stream)
+
+    def write(self, stream=None):
+        B.reshape_and_cache(self.new_key, self.new_value, self.key_cache, self.value_cache,
+                            self.slot_mapping, block_size=self.block_size,
+                            num_blocks=self.num_blocks, stream=stream)
+
+    def attend(self, stream=None):
+        B.paged_attention_decode(self.out, self.query, self.key_cache, self.value_cache,
+                                 self.block_tables, self.context_lens,
+                                 num_kv_heads=self.num_kv_heads, block_size=self.block_size,
+                                 max_context_len=self.max_context_len, scale=self.scale,
+                                 partition_size=self.partition_size, workspace=self.workspace,
+                                 num_blocks=self.num_blocks, stream=stream)
+
+    def run(self, stream=None):
+        self.copy(stream)
+        self.write(stream)
+        self.attend(stream)
+        return self.out
+
+
+def _finish(query, key_cache, value_cache, new_key, new_value, slots, pairs, tables, lens, *,
+            num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+            out_dtype=None) -> DecodeStep:
+    import torch
+    dev = query.device
+    t_slots = torch.as_tensor(np.ascontiguousarray(slots, dtype=np.int64)).to(dev)
+    t_pairs = torch.as_tensor(np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)).to(dev)
+    t_tab = torch.as_tensor(np.ascontiguousarray(tables, dtype=np.int32)).to(dev)
+    t_lens = torch.as_tensor(np.ascontiguousarray(lens, dtype=np.int32)).to(dev)
+    mcl = int(np.max(lens)) if len(lens) else 0
+    out = torch.empty(query.shape, dtype=out_dtype or query.dtype, device=dev)
+    nbytes = B.paged_attention_workspace_bytes(query.shape[0], query.shape[1], head_dim, mcl,
+                                               partition_size)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    return DecodeStep(query, key_cache, value_cache, new_key, new_value, t_slots, t_pairs, t_tab,
+                      t_lens, out, ws, num_kv_heads, head_dim, block_size, num_blocks, mcl, scale,
+                      partition_size)
+
+
+def step_from_case(case, partition_size: int, out_dtype=None) -> DecodeStep:
+    """A step over a workload whose tables are given: write the token at
+    position L-1 of each sequence, then attend over all L tokens."""
+    return _finish(case.query, case.key_cache, case.value_cache, case.new_key, case.new_value,
+                   case.slot_mapping, np.zeros((0, 2), np.int64), case.block_tables,
+                   case.context_lens, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                   block_size=case.block_size, num_blocks=case.num_blocks, scale=case.scale,
+                   partition_size=partition_size, out_dtype=out_dtype)
+
+
+SHADOW = 1 << 40   # shadow sequence ids: seq_id + SHADOW
+
+
+def build_shared_prefix_state(plan) -> "B.BlockAllocator":
+    """Allocator state before the step: one prompt, batch-1 forks, private tails."""
+    a = B.BlockAllocator(plan.num_blocks, plan.block_size, plan.perm)
+    a.create(0, int(plan.prompt))
+    for i in range(1, plan.batch):
+        a.fork(0, i)
+    for i in range(plan.batch):
+        for _ in range(int(plan.tails[i])):
+            a.append_slot(i)
+    return a
+
+
+def shared_prefix_step(plan, tensors, partition_size: int, out_dtype=None):
+    """The shared-prefix sampling step: fork every sequence into a shadow
+    that shares all its blocks (beam-search style), append one token to each
+    sequence in ascending id (copy-on-write where the last block is partial
+    and shared), then free the shadows.  Returns (step, host record)."""
+    a = build_shared_prefix_state(plan)
+    for i in range(plan.batch):
+        a.fork(i, SHADOW + i)
+    slots = np.empty(plan.batch, np.int64)
+    pairs = []
+    for i in range(plan.batch):
+        s, src, dst = a.append_slot(i)
+        slots[i] = s
+        if src >= 0:
+            pairs.append((src, dst))
+    for i in range(plan.batch):
+        a.free(SHADOW + i)
+    lens = np.array([a.seq_len(i) for i in range(plan.batch)], np.int64)
+    max_blocks = int(-(-lens.max() // plan.block_size))
+    tables, lens32 = a.build_block_tables(list(range(plan.batch)), max_blocks)
+    pairs = np.array(pairs, np.int64).reshape(-1, 2)
+    step = _finish(tensors["query"], tensors["key_cache"], tensors["value_cache"],
+                   tensors["new_key"], tensors["new_value"], slots, pairs, tables, lens32,
+                   num_kv_heads=tensors["num_kv_heads"], head_dim=tensors["head_dim"],
+                   block_size=plan.block_size, num_blocks=plan.num_blocks,
+                   scale=tensors["scale"], partition_size=partition_size, out_dtype=out_dtype)
+    record = dict(slots=slots, pairs=pairs, tables=tables, lens=lens32, allocator=a)
+    return step, record

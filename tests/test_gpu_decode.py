@@ -1,0 +1,206 @@
+"""paged_attention_decode on the GPU against the CPU oracle (same tensors).
+
+Tolerance: max-abs 1e-5 for fp32 KV, 2e-2 for bf16 KV (fp32 accumulation).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import pool_layout as pl
+from tests.gpu_helpers import TOL, gpu_decode, max_abs_err, oracle_decode, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(pa, case, ps, out_dtype=None, idx=None):
+    out = gpu_decode(pa, case, partition_size=ps, out_dtype=out_dtype)
+    ref = oracle_decode(case, idx=idx)
+    got = out if idx is None else out[torch.as_tensor(idx, device="cuda")]
+    err = max_abs_err(got, ref)
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL[case.dtype], "max abs err %.3g (tol %.1g)" % (err, TOL[case.dtype])
+    return out, err
+
+
+# Small cases: every path and shape, several tiles, ragged tails, L = 1.
+SMALL = [
+    ("tiny", {}),
+    ("7b", dict(batch=6, len_range=(1, 300))),
+    ("7b", dict(batch=5, lens=(1, 16, 17, 1100, 255))),            # >64 blocks: 2 table chunks
+    ("70b", dict(batch=6, len_range=(1, 700))),
+    ("70b", dict(batch=3, len_range=(100, 400), block_size=32)),
+    ("long", dict(batch=2, lens=(3000, 1500))),
+    ("long", dict(batch=2, lens=(3000, 1501), block_size=32)),
+    ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=8, num_kv_heads=4)),    # G = 2
+    ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=16, num_kv_heads=1)),   # G = 16
+    ("7b", dict(batch=3, len_range=(1, 200), num_q_heads=64, num_kv_heads=2)),   # G = 32
+    ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=24, num_kv_heads=8,
+                head_dim=64)),                                                  # G = 3, d 64
+    ("7b", dict(batch=4, len_range=(1, 200), head_dim=64, num_q_heads=4, num_kv_heads=4)),
+    ("tiny", dict(num_q_heads=8, num_kv_heads=2, lens=(5, 40, 64, 129), pool=40)),  # fp32 GQA
+    ("tiny", dict(head_dim=128, block_size=32, lens=(1, 31, 33, 90))),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL)
+@pytest.mark.parametrize("ps", [0, "bs", 64, 512])
+def test_small_cases_match_oracle(gpu, name, kw, ps):
+    case = W.make_case(name, device="cuda", **kw)
+    ps = case.block_size if ps == "bs" else ps
+    if ps and ps % case.block_size:
+        pytest.skip("partition size must be a multiple of the block size")
+    _check(gpu, case, ps)
+
+
+@pytest.mark.parametrize("name,kw", [("7b", dict(batch=3, len_range=(1, 300))),
+                                     ("70b", dict(batch=3, len_range=(1, 300))),
+                                     ("tiny", {})])
+def test_fp32_and_bf16_outputs(gpu, name, kw):
+    case = W.make_case(name, device="cuda", **kw)
+    for od in (torch.float32, torch.bfloat16):
+        _check(gpu, case, 64, out_dtype=od)
+
+
+# Full-size workloads, launched as the benchmark launches them, checked on
+# sampled sequences the oracle computes one by one.
+FULL = [("7b", {}, 512), ("70b", {}, 512), ("long", {}, 512), ("long", dict(block_size=32), 512),
+        ("7b", {}, 0)]
+
+
+@pytest.mark.parametrize("name,kw,ps", FULL)
+def test_full_size_workloads_on_sampled_sequences(gpu, name, kw, ps):
+    case = W.make_case(name, device="cuda", **kw)
+    idx = np.sort(np.random.default_rng(7).choice(case.batch, size=min(6, case.batch),
+                                                  replace=False))
+    _check(gpu, case, ps, idx=idx)
+
+
+def test_empty_sequences_give_zero_rows(gpu):
+    case = W.make_case("70b", device="cuda", batch=4, len_range=(20, 90))
+    lens = case.context_lens.copy()
+    lens[[1, 3]] = 0
+    for ps in (0, 32):
+        out = gpu_decode(gpu, case, partition_size=ps, lens=lens)
+        assert torch.all(out[[1, 3]] == 0)
+        ref = oracle_decode(case, lens=lens)
+        assert max_abs_err(out, ref) <= TOL["bf16"]
+
+
+def test_permuting_physical_blocks_is_bit_identical(gpu):
+    for name, kw in (("7b", dict(batch=4, len_range=(40, 400))),
+                     ("70b", dict(batch=4, len_range=(40, 400))),
+                     ("tiny", {})):
+        case = W.make_case(name, device="cuda", **kw)
+        base = gpu_decode(gpu, case, partition_size=64)
+        pi = torch.from_numpy(np.random.default_rng(3).permutation(case.num_blocks)).cuda()
+        kc = torch.empty_like(case.key_cache); kc[pi] = case.key_cache
+        vc = torch.empty_like(case.value_cache); vc[pi] = case.value_cache
+        tab = pi.cpu().numpy()[case.block_tables].astype(np.int32)
+        moved = gpu_decode(gpu, case, partition_size=64, tables=tab, key_cache=kc, value_cache=vc)
+        assert torch.equal(base, moved)
+
+
+def test_shared_prefix_blocks_give_bit_identical_outputs(gpu):
+    """Seq 0 holds private copies of a 3-block prefix; seq 1 reads seq 2's blocks."""
+    case = W.make_case("70b", device="cuda", batch=3, lens=(48 + 21, 48 + 21, 48 + 9), pool=20)
+    tab = case.block_tables.copy()
+    tab[1, :3] = tab[2, :3]
+    kc, vc = case.key_cache.clone(), case.value_cache.clone()
+    t0 = torch.as_tensor(case.block_tables[0], device="cuda").long()
+    t1 = torch.as_tensor(tab[1], device="cuda").long()
+    kc[t1[:3]] = kc[t0[:3]]; vc[t1[:3]] = vc[t0[:3]]
+    kc[t1[3:5]] = kc[t0[3:5]]; vc[t1[3:5]] = vc[t0[3:5]]
+    q = case.query.clone(); q[1] = q[0]
+    for ps in (0, 16, 32):
+        out = gpu_decode(gpu, case, partition_size=ps, tables=tab, key_cache=kc, value_cache=vc,
+                         query=q)
+        assert torch.equal(out[0], out[1])
+
+
+def _host_pools(case):
+    """Host copies of the pools viewed in the library layout."""
+    dt = np.uint16 if case.dtype == "bf16" else np.float32
+    x = 16 // np.dtype(dt).itemsize
+    kp = W.host_array(case.key_cache).reshape(case.num_blocks, case.num_kv_heads,
+                                              case.head_dim // x, case.block_size, x)
+    vp = W.host_array(case.value_cache).reshape(case.num_blocks, case.num_kv_heads,
+                                                case.head_dim, case.block_size)
+    return kp, vp, dt
+
+
+def _pool_to_dev(arr, like):
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16 if arr.dtype == np.uint16
+                                                        else arr.dtype))
+    return t.cuda().view(like.dtype).view(like.shape)
+
+
+def _poisoned(case):
+    """Device pools where every slot not holding a live token is NaN."""
+    kp, vp, dt = _host_pools(case)
+    nan = np.uint16(0x7FC0) if dt == np.uint16 else np.float32(np.nan)
+    nk, nv = pl.empty_pools(case.num_blocks, case.num_kv_heads, case.head_dim, case.block_size,
+                            dt, fill=nan)
+    for i, L in enumerate(case.context_lens):
+        k, v = pl.gather_sequence(kp, vp, case.block_tables[i], int(L), case.block_size)
+        pl.scatter_sequences(nk, nv, case.block_tables[i:i + 1], [k], [v], case.block_size,
+                             fill=nan)
+    return _pool_to_dev(nk, case.key_cache), _pool_to_dev(nv, case.value_cache)
+
+
+def test_nan_poisoned_pool_and_bad_padding_entries_are_never_used(gpu):
+    for name, kw in (("7b", dict(batch=5, len_range=(1, 150))),
+                     ("70b", dict(batch=5, len_range=(1, 150))),
+                     ("70b", dict(batch=3, len_range=(1, 150), block_size=32)),
+                     ("tiny", {})):
+        case = W.make_case(name, device="cuda", **kw)
+        kc, vc = _poisoned(case)
+        tab = case.block_tables.copy()
+        for i, L in enumerate(case.context_lens):
+            tab[i, -(-int(L) // case.block_size):] = case.num_blocks + 1000 + i
+        clean = gpu_decode(gpu, case, partition_size=32)
+        for ps in (0, 32):
+            out = gpu_decode(gpu, case, partition_size=ps, tables=tab, key_cache=kc,
+                             value_cache=vc)
+            assert torch.isfinite(out.float()).all()
+            if ps == 32:
+                assert torch.equal(out, clean)
+
+
+def test_run_to_run_determinism(gpu):
+    case = W.make_case("70b", device="cuda", batch=8, len_range=(100, 1200))
+    outs = [gpu_decode(gpu, case, partition_size=256) for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    case = W.make_case("7b", device="cuda", batch=8, len_range=(100, 1200))
+    outs = [gpu_decode(gpu, case, partition_size=0) for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_deep_validation_rejects_bad_tables_without_launching(gpu, monkeypatch):
+    case = W.make_case("70b", device="cuda", batch=3, len_range=(20, 60))
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    ok = gpu_decode(gpu, case, partition_size=16)
+    bad = case.block_tables.copy()
+    bad[1, 0] = case.num_blocks
+    sentinel = torch.full_like(ok, 7.0)
+    with pytest.raises(gpu.PagedAttnError) as e:
+        gpu.paged_attention_decode(sentinel, case.query, case.key_cache, case.value_cache,
+                                   to_dev(bad), to_dev(case.context_lens),
+                                   num_kv_heads=case.num_kv_heads, block_size=16,
+                                   max_context_len=int(case.context_lens.max()),
+                                   scale=case.scale, partition_size=16,
+                                   num_blocks=case.num_blocks)
+    assert e.value.status == gpu.PA_ERR_INVALID_ARG
+    lens = case.context_lens.copy()
+    lens[0] = int(lens.max()) + 1
+    with pytest.raises(gpu.PagedAttnError):
+        gpu.paged_attention_decode(sentinel, case.query, case.key_cache, case.value_cache,
+                                   to_dev(case.block_tables), to_dev(lens),
+                                   num_kv_heads=case.num_kv_heads, block_size=16,
+                                   max_context_len=int(case.context_lens.max()),
+                                   scale=case.scale, partition_size=16,
+                                   num_blocks=case.num_blocks)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)

@@ -202,11 +202,14 @@ def make_case(name: str, device="cpu", **overrides) -> DecodeCase:
 
     ``batch``/``lens``/``len_range``/``block_size``/``pool``/``seed`` override
     the workload's values to get the same shape at a size the oracle finishes
-    in seconds.  The shared-prefix workload is built by ``shared_plan`` and
+    in seconds; ``num_q_heads``/``num_kv_heads``/``head_dim``/``dtype`` give
+    other head shapes with the same structure.  The shared-prefix workload is built by ``shared_plan`` and
     ``shared_tensors``.
     """
+    shape = {k: overrides.pop(k) for k in ("num_q_heads", "num_kv_heads", "head_dim", "dtype")
+             if k in overrides}
     st = case_structure(name, **overrides)
-    cfg = CONFIGS[name]
+    cfg = {**CONFIGS[name], **shape}
     hq, hkv, d, dt = cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["dtype"]
     bs, n_blocks = st.block_size, st.num_blocks
     gen = torch.Generator(device=device).manual_seed(st.seed)
