@@ -9,8 +9,9 @@ new token, and paged_attention_decode over all cached tokens (main kernel,
 plus the log-sum-exp merge when a sequence spans several partitions).
 
 Timing: W warm-up steps, then K timed steps.  Before each step a 1 GiB
-buffer is written to evict the L2s and the Infinity Cache (outside the
-events).  Each step is bracketed by HIP events on the stream the kernels
+buffer is read to evict the L2s and the Infinity Cache (outside the
+events); reading leaves only clean lines behind, so no write-back of the
+flush competes with the step.  Each step is bracketed by HIP events on the stream the kernels
 run on; the main attention kernel is bracketed by its own pair of events,
 recorded by the library right around its launch.
 
@@ -182,23 +183,27 @@ def main():
     step, lens, info = build_step(args.workload, args.partition_size, device)
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=device)
     K, W_ = args.steps, args.warmup
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # torch creates the HIP event on first record; the library re-records it
+        return e
     s_ev, e_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
     ms_ev, me_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
+    torch.cuda.synchronize()
 
     log("warmup %d steps" % W_)
     for _ in range(W_):
         if flush is not None:
-            flush.zero_()
+            flush.sum()
         step.run()
     torch.cuda.synchronize()
     log("timing %d steps" % K)
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
-            flush.zero_()
+            flush.sum()
         pa.set_timing_events(ms_ev[i], me_ev[i])
         s_ev[i].record()
         step.run()

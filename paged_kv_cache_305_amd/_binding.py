@@ -179,7 +179,12 @@ def allocate_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device
 def set_timing_events(before_main=None, after_main=None):
     """Record these torch.cuda.Events around the main attention kernel of every
     later decode call (None, None stops)."""
-    h = lambda e: None if e is None else int(e.cuda_event)
+    def h(e):
+        if e is None:
+            return None
+        if not int(e.cuda_event):
+            raise ValueError("record the event once first: torch creates HIP events lazily")
+        return int(e.cuda_event)
     _check(load().pa_set_timing_events(h(before_main), h(after_main)))
 
 

@@ -46,7 +46,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short mfma_i16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float mfma_f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPrefetch = 2;   // tiles of K/V loads kept in flight per wave
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 2
+#endif
+constexpr int kPrefetch = PA_PREFETCH;   // tiles of K/V loads kept in flight per wave
 
 struct bf16_t {
   uint16_t bits;
@@ -232,8 +235,14 @@ struct TableReader {
 // loads 16-byte row segments (rows j*RPI + l/LPR, tokens X*(l%LPR)..+X) and
 // reads those tokens' probabilities from LDS.
 
+#ifdef PA_WAVES_PER_EU
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_OCCUPANCY
+#endif
+
 template <typename KV, int D, int BS, typename OUT>
-__global__ __launch_bounds__(64) void decode_valu(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_valu(Params p) {
   constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
   constexpr int KJ = D / X / 4;             // key chunks per lane per tile
   constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(64) void decode_valu(Params p) {
 // accumulators are rescaled by each lane's own factor.
 
 template <int D, int BS, typename OUT>
-__global__ __launch_bounds__(64) void decode_mfma(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_mfma(Params p) {
   constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   constexpr int VT = D / 16;   // 16-feature output tiles
   constexpr int TPB = BS / 16;

@@ -19,10 +19,15 @@ def _check(pa, case, ps, out_dtype=None, idx=None):
     out = gpu_decode(pa, case, partition_size=ps, out_dtype=out_dtype)
     ref = oracle_decode(case, idx=idx)
     got = out if idx is None else out[torch.as_tensor(idx, device="cuda")]
-    err = max_abs_err(got, ref)
     assert torch.isfinite(out.float()).all()
-    assert err <= TOL[case.dtype], "max abs err %.3g (tol %.1g)" % (err, TOL[case.dtype])
-    return out, err
+    diff = np.abs(got.double().cpu().numpy() - ref)
+    # A bf16 output is the fp32 result rounded to nearest even: on top of the
+    # accumulation tolerance it may differ by half a bf16 ulp.  bf16 keeps 8
+    # significant bits, so half an ulp is at most 2^-8 |ref|.
+    bound = TOL[case.dtype] + (2.0 ** -8 * np.abs(ref) if out.dtype == torch.bfloat16 else 0.0)
+    worst = float(np.max(diff - bound)) if diff.size else -1.0
+    assert worst <= 0, "max abs err %.3g exceeds tolerance by %.3g" % (float(diff.max()), worst)
+    return out, float(diff.max()) if diff.size else 0.0
 
 
 # Small cases: every path and shape, several tiles, ragged tails, L = 1.
@@ -204,3 +209,28 @@ def test_deep_validation_rejects_bad_tables_without_launching(gpu, monkeypatch):
                                    num_blocks=case.num_blocks)
     torch.cuda.synchronize()
     assert torch.all(sentinel == 7.0)
+
+
+def test_timing_hook_brackets_the_main_kernel(gpu):
+    case = W.make_case("70b", device="cuda", batch=16, len_range=(500, 2000))
+    from paged_kv_cache_305_amd.step import step_from_case
+    step = step_from_case(case, partition_size=256)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        gpu.set_timing_events(torch.cuda.Event(enable_timing=True), evs[1])
+    gpu.set_timing_events(evs[1], evs[2])
+    try:
+        evs[0].record()
+        step.run()
+        evs[3].record()
+        torch.cuda.synchronize()
+    finally:
+        gpu.set_timing_events(None, None)
+    main = evs[1].elapsed_time(evs[2])
+    whole = evs[0].elapsed_time(evs[3])
+    assert 0 < main <= whole
+    ref = oracle_decode(case, idx=[0, 5])
+    assert max_abs_err(step.out[[0, 5]], ref) <= TOL["bf16"]
