@@ -153,7 +153,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="tokens per split-K partition; 0 = none, -1 = balanced split")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -221,8 +222,9 @@ def main():
     B = int(step.query.shape[0])
     gbs = kv_bytes / t_step / 1e9
     achieved = attn_bytes / t_main / 1e9
-    kernel = "decode_mfma" if (step.query.dtype == torch.bfloat16 and
-                              step.query.shape[1] // step.num_kv_heads >= 2) else "decode_valu"
+    body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
+                          step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
+    kernel = "%s<%s>" % ("decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
     roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=counter_traffic(args.workload, args.partition_size),
@@ -242,6 +244,7 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block permutation)",
         "config": {"workload": WORKLOADS[args.workload], "partition_size": args.partition_size,
                    "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
+                   "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
                    "flush_between_steps": flush is not None, **info},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / t_step, 1),

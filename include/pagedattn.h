@@ -57,6 +57,18 @@ typedef int32_t pa_dtype;
 #define PA_FP32 0
 #define PA_BF16 1
 
+/* partition_size of pa_paged_attention_decode: balanced split. */
+#define PA_PARTITION_BALANCED (-1)
+
+/* flags of pa_paged_attention_decode.
+ * PA_DECODE_KV_REUSED: some physical blocks are read by more than one
+ *   sequence in this call (a shared prefix).  The K/V loads then go through
+ *   the caches so repeated reads hit, and a balanced split keeps each KV
+ *   head on one XCD.  Without it every block is streamed past the caches
+ *   (non-temporal loads), the fastest choice when each block is read once.
+ *   Results are the same either way. */
+#define PA_DECODE_KV_REUSED 1u
+
 /* Message describing the last error on the calling thread ("" if none). */
 const char *pa_last_error(void);
 
@@ -86,10 +98,16 @@ int32_t pa_version(void);
  *  scale          multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
  *  max_context_len  host upper bound of every L_i; sizes the launch without
  *                 a device read.  Must be <= max_blocks_per_seq * block_size.
- *  partition_size 0: one pass per (sequence, head).  Otherwise a positive
- *                 multiple of block_size: each sequence's context is split
- *                 into ceil(L_i / partition_size) partitions computed
- *                 independently and merged exactly by a log-sum-exp reduce.
+ *  partition_size how each sequence's context is split across waves; the
+ *                 pieces are merged exactly by a log-sum-exp reduce:
+ *                   > 0  a multiple of block_size: ceil(L_i / partition_size)
+ *                        partitions of that many tokens;
+ *                   0    no split, one pass per (sequence, head);
+ *                   < 0  (PA_PARTITION_BALANCED) balanced: the tiles of all
+ *                        sequences are cut into one range per wave the GPU
+ *                        holds at once, sized per XCD by
+ *                        pa_set_balance_weights.
+ *  flags          PA_DECODE_* bits (0: K/V streamed, each block read once).
  *  workspace      device scratch of at least
  *                 pa_paged_attention_workspace_bytes(...) bytes when that is
  *                 nonzero (caller-owned, contents need not be initialised).
@@ -104,7 +122,8 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                                     int32_t block_size, int32_t max_blocks_per_seq,
                                     int64_t num_blocks, int32_t max_context_len, float scale,
                                     int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+                                    uint32_t flags, void *workspace, size_t workspace_bytes,
+                                    void *stream);
 
 /* Tracing hook: while set, every pa_paged_attention_decode call records
  * hipEvent_t `before_main` just before its main attention kernel and
@@ -114,12 +133,23 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
  * thread-safe.  Used to time the main kernel alone. */
 pa_status pa_set_timing_events(void *before_main, void *after_main);
 
-/* Bytes of workspace pa_paged_attention_decode needs for these sizes; 0 when
- * no sequence can have more than one partition.  Returns 0 for invalid
- * arguments too (the decode call then reports them). */
+/* Tile shares of the balanced split (partition_size < 0), one weight per XCD
+ * in workgroup dispatch order (workgroup w runs on XCD w mod 8): each wave's
+ * range of tiles is proportional to its XCD's weight.  Default
+ * {110,100,110,100,110,100,110,100}: on MI355X, waves on even-numbered XCDs
+ * stream about 10% faster than waves on odd-numbered ones.  weights == NULL
+ * restores the default; otherwise n must be 8 and each weight in [1, 1000].
+ * Process-wide; affects performance only, never results. */
+pa_status pa_set_balance_weights(const int32_t *weights, int32_t n);
+
+/* Bytes of workspace pa_paged_attention_decode needs for these sizes on the
+ * current device; 0 when every output row is written directly (no split).
+ * Returns 0 for invalid arguments too (the decode call then reports them),
+ * and for a balanced split when no device can be queried. */
 size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                          int32_t head_dim, int32_t max_context_len,
-                                          int32_t partition_size);
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          pa_dtype kv_dtype);
 
 /* ------------------------------------------------------------------------
  * reshape_and_cache -- write each new token's K/V into its slot of the

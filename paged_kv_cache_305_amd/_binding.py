@@ -26,11 +26,14 @@ PA_ERR_UNKNOWN_SEQ = -4
 PA_ERR_HIP = -5
 PA_FP32 = 0
 PA_BF16 = 1
+PA_PARTITION_BALANCED = -1
+PA_DECODE_KV_REUSED = 1
 
 # Every symbol include/pagedattn.h declares.
 EXPORTS = (
     "pa_last_error", "pa_version",
     "pa_paged_attention_decode", "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
+    "pa_set_balance_weights",
     "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free",
     "pa_allocator_block_size", "pa_seq_create", "pa_seq_fork", "pa_seq_append_slot",
@@ -56,9 +59,11 @@ def _declare(lib):
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_version": (i32, []),
         "pa_paged_attention_decode": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                            i64, i32, f32, i32, i32, i32, vp, sz, vp]),
-        "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+                                            i64, i32, f32, i32, i32, i32, ctypes.c_uint32, vp, sz,
+                                            vp]),
+        "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_set_timing_events": (i32, [vp, vp]),
+        "pa_set_balance_weights": (i32, [vp, i32]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_allocator_create": (vp, [i64, i32, vp]),
@@ -188,17 +193,35 @@ def set_timing_events(before_main=None, after_main=None):
     _check(load().pa_set_timing_events(h(before_main), h(after_main)))
 
 
-def paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                    partition_size) -> int:
-    return int(load().pa_paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                         max_context_len, partition_size))
+def set_balance_weights(weights=None):
+    """Per-XCD tile shares of the balanced split (8 ints in [1, 1000]); None restores
+    the default (even-numbered XCDs 110, odd 100)."""
+    if weights is None:
+        _check(load().pa_set_balance_weights(None, 0))
+        return
+    w = np.ascontiguousarray(np.asarray(weights, dtype=np.int32))
+    _check(load().pa_set_balance_weights(w.ctypes.data, int(w.size)))
+
+
+def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    max_context_len, partition_size, kv_dtype) -> int:
+    """kv_dtype: PA_FP32 / PA_BF16 or a torch dtype."""
+    code = kv_dtype if isinstance(kv_dtype, int) else \
+        {_torch().float32: PA_FP32, _torch().bfloat16: PA_BF16}[kv_dtype]
+    return int(load().pa_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                         head_dim, max_context_len,
+                                                         partition_size, code))
 
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, *,
                            num_kv_heads: int, block_size: int, max_context_len: int,
                            scale: float, partition_size: int = 0, workspace=None,
-                           num_blocks: Optional[int] = None, stream=None):
-    """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables."""
+                           num_blocks: Optional[int] = None, kv_reused: bool = False,
+                           stream=None):
+    """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables.
+
+    kv_reused: some physical blocks are read by several sequences (shared
+    prefixes): keep K/V in the caches instead of streaming them."""
     lib = load()
     dev = query.device
     for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
@@ -221,7 +244,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     chunk = num_kv_heads * d * block_size
     if key_cache.numel() < nb * chunk or value_cache.numel() < nb * chunk:
         raise ValueError("pools hold fewer than num_blocks blocks")
-    need = paged_attention_workspace_bytes(B, hq, d, max_context_len, partition_size)
+    need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
+                                           partition_size, query.dtype)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (
@@ -230,7 +254,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
         out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
         int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
-        _dtype_code(query), _dtype_code(out), ws_ptr, ws_bytes, _stream(dev, stream)))
+        _dtype_code(query), _dtype_code(out), PA_DECODE_KV_REUSED if kv_reused else 0, ws_ptr,
+        ws_bytes, _stream(dev, stream)))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <unordered_set>
 #include <vector>
 
@@ -38,32 +39,83 @@ pa_status to_host(std::vector<T> &dst, const T *src, size_t n, void *stream) {
 void *g_ev_before_main = nullptr;
 void *g_ev_after_main = nullptr;
 
+// Per-XCD tile shares of the balanced split.  Measured on MI355X: waves on
+// even-numbered XCDs finish a fixed share about 10% sooner than waves on
+// odd-numbered ones, so equal shares leave the even XCDs idle at the end.
+constexpr int32_t kDefaultXcdWeights[8] = {110, 100, 110, 100, 110, 100, 110, 100};
+std::atomic<int32_t> g_xcd_weights[8] = {110, 100, 110, 100, 110, 100, 110, 100};
+
 int32_t partitions_for(int32_t max_context_len, int32_t partition_size) {
   if (partition_size <= 0) return 1;
   const int32_t n = (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size);
   return n > 0 ? n : 1;
 }
 
+// Most waves a balanced launch may use on the current device: 32 per
+// compute unit (the wave slots of a gfx950 CU).  0 if no device answers.
+int32_t balanced_wave_bound() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus * 32;
+}
+
+// Partial rows a call needs (0: it writes every output row directly).  A
+// balanced call is sized for the largest plan it can take on this device.
+size_t partial_rows(int32_t num_seqs, const pa::HeadUnits &hu, int32_t max_context_len,
+                    int32_t partition_size, int32_t wave_bound) {
+  if (partition_size < 0) {
+    pa::DecodeArgs a{};
+    a.num_seqs = num_seqs;
+    a.max_context_len = max_context_len;
+    a.max_waves = wave_bound;
+    a.flags = PA_DECODE_KV_REUSED;   // rows do not depend on the split; take the widest
+    return pa::balanced_plan(a, hu.units, wave_bound).rows * hu.gu;
+  }
+  const int32_t parts = partitions_for(max_context_len, partition_size);
+  if (parts <= 1) return 0;
+  return (size_t)num_seqs * hu.units * parts * hu.gu;
+}
+
 }  // namespace
 
 namespace pa {
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t num_partitions) {
-  WorkspaceLayout w{0, 0, 0, 0};
-  if (num_partitions <= 1 || num_seqs <= 0 || num_q_heads <= 0) return w;
-  const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions;
+void balance_weights(int32_t out[8]) {
+  for (int i = 0; i < 8; ++i) out[i] = g_xcd_weights[i].load(std::memory_order_relaxed);
+}
+
+WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments) {
+  WorkspaceLayout w{rows, 0, 0, 0, 0, 0};
+  if (rows == 0) return w;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  w.max_off = 0;
   w.sum_off = up(rows * sizeof(float));
   w.acc_off = w.sum_off + up(rows * sizeof(float));
-  w.total = w.acc_off + up(rows * (size_t)head_dim * sizeof(float));
+  w.seg_off = w.acc_off + up(rows * (size_t)head_dim * sizeof(float));
+  w.total = w.seg_off + up(segments * 2 * sizeof(int32_t));
   return w;
 }
 
 }  // namespace pa
 
 extern "C" {
+
+pa_status pa_set_balance_weights(const int32_t *weights, int32_t n) {
+  pa_clear_error();
+  if (weights == nullptr) {
+    for (int i = 0; i < 8; ++i) g_xcd_weights[i].store(kDefaultXcdWeights[i]);
+    return PA_OK;
+  }
+  if (n != 8)
+    return pa_fail(PA_ERR_INVALID_ARG, "pa_set_balance_weights: expected 8 weights, got %d", n);
+  for (int i = 0; i < 8; ++i)
+    if (weights[i] < 1 || weights[i] > 1000)
+      return pa_fail(PA_ERR_INVALID_ARG, "pa_set_balance_weights: weight %d = %d outside [1, 1000]",
+                     i, weights[i]);
+  for (int i = 0; i < 8; ++i) g_xcd_weights[i].store(weights[i]);
+  return PA_OK;
+}
 
 pa_status pa_set_timing_events(void *before_main, void *after_main) {
   pa_clear_error();
@@ -75,13 +127,19 @@ pa_status pa_set_timing_events(void *before_main, void *after_main) {
 }
 
 size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                          int32_t head_dim, int32_t max_context_len,
-                                          int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
-      partition_size < 0)
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          pa_dtype kv_dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_context_len < 0 ||
+      elem_bytes(kv_dtype) == 0)
     return 0;
-  return pa::workspace_layout(num_seqs, num_q_heads, head_dim,
-                              partitions_for(max_context_len, partition_size))
+  const pa::HeadUnits hu = pa::head_units(num_q_heads, num_kv_heads, kv_dtype);
+  const int32_t bound = partition_size < 0 ? balanced_wave_bound() : 0;
+  if (partition_size < 0 && bound == 0) return 0;
+  return pa::workspace_layout(
+             partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
+             partition_size < 0 ? (size_t)num_seqs * hu.units : 0)
       .total;
 }
 
@@ -92,7 +150,8 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                                     int32_t block_size, int32_t max_blocks_per_seq,
                                     int64_t num_blocks, int32_t max_context_len, float scale,
                                     int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+                                    uint32_t flags, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
   pa_clear_error();
   const char *fn = "pa_paged_attention_decode";
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
@@ -113,10 +172,12 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
     return pa_fail(PA_ERR_INVALID_ARG,
                    "%s: max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]",
                    fn, max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % block_size != 0))
+  if (partition_size > 0 && partition_size % block_size != 0)
     return pa_fail(PA_ERR_INVALID_ARG,
-                   "%s: partition_size %d must be 0 or a positive multiple of block_size %d", fn,
-                   partition_size, block_size);
+                   "%s: partition_size %d must be negative (balanced), 0, or a positive "
+                   "multiple of block_size %d", fn, partition_size, block_size);
+  if ((flags & ~PA_DECODE_KV_REUSED) != 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -124,7 +185,13 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
     return pa_fail(PA_ERR_INVALID_ARG, "%s: out, query and pools must be 16-byte aligned", fn);
 
   const int32_t parts = partitions_for(max_context_len, partition_size);
-  const pa::WorkspaceLayout ws = pa::workspace_layout(num_seqs, num_q_heads, head_dim, parts);
+  const pa::HeadUnits hu = pa::head_units(num_q_heads, num_kv_heads, kv_dtype);
+  const int32_t bound = partition_size < 0 ? balanced_wave_bound() : 0;
+  if (partition_size < 0 && bound == 0)
+    return pa_fail(PA_ERR_HIP, "%s: cannot query the current device", fn);
+  const pa::WorkspaceLayout ws = pa::workspace_layout(
+      partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
+      partition_size < 0 ? (size_t)num_seqs * hu.units : 0);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu", fn,
@@ -171,12 +238,16 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
   a.scale = scale;
   a.partition_size = partition_size;
   a.num_partitions = parts;
+  a.max_waves = bound;
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
+  a.flags = flags;
   char *wsb = static_cast<char *>(workspace);
   a.ws_max = ws.total ? reinterpret_cast<float *>(wsb + ws.max_off) : nullptr;
   a.ws_sum = ws.total ? reinterpret_cast<float *>(wsb + ws.sum_off) : nullptr;
   a.ws_acc = ws.total ? reinterpret_cast<float *>(wsb + ws.acc_off) : nullptr;
+  a.seg_units = ws.total ? reinterpret_cast<int32_t *>(wsb + ws.seg_off) : nullptr;
+  pa::balance_weights(a.xcd_weights);
   a.ev_before_main = g_ev_before_main;
   a.ev_after_main = g_ev_after_main;
   const int e = pa::launch_decode(a, stream);

@@ -8,24 +8,39 @@
 // paragraph).  Query head h reads KV head h / G, G = Hq / Hkv (same
 // glossary, GQA paragraph).
 //
-// Work unit: one wave64 workgroup per (sequence, head unit, context
-// partition).  A partition is `partition_size` tokens (or the whole context
-// when it is 0); partitions of a sequence are merged exactly by a
-// log-sum-exp reduce (decode_reduce) when there is more than one.
+// The work is cut into segments, one per (sequence, head unit), each a run
+// of 16-token tiles (a 32-token block is two tiles).  A wave64 processes a
+// piece -- a contiguous tile range of one segment -- keeping the running
+// max / sum / output in registers and PF tiles of K/V loads in flight.  A
+// piece covering its whole segment writes the output row; any other piece
+// writes a partial (max, sum, unnormalised output) that decode_merge
+// combines exactly by log-sum-exp.
 //
-// Two main kernels, chosen per call:
-//  * decode_valu -- head unit = one query head.  Vector-ALU dot products;
-//    used for MHA (G = 1) and for fp32 KV.
-//  * decode_mfma -- head unit = one KV head and up to 16 of its query heads.
-//    bf16 KV with G >= 2: Q.K^T and P.V run on v_mfma_f32_16x16x32_bf16 and
+// Head units, chosen per call:
+//  * VALU body -- one query head.  Vector-ALU dot products; used for MHA
+//    (G = 1) and for fp32 KV.
+//  * MFMA body -- one KV head and up to 16 of its query heads.  bf16 KV with
+//    G >= 2: Q.K^T and P.V run on v_mfma_f32_16x16x32_bf16 and
 //    v_mfma_f32_16x16x16_bf16 with the group's query heads on the N side of
 //    both products, so each KV byte is read once for the whole group.
 //
-// Both kernels walk the partition in 16-token tiles (a block of 32 tokens is
-// two tiles), keep PF tiles of K/V loads in flight in registers, keep the
-// running max / sum / output in registers, and fix every reduction order
-// by logical token position, so results are deterministic and independent
-// of where the blocks sit physically.
+// How segments become pieces:
+//  * fixed partitions (partition_size > 0, or 0 = whole segment): one
+//    workgroup per (unit, sequence, partition);
+//  * balanced (partition_size < 0): exactly as many waves as the GPU holds
+//    at once; the tiles of all segments, laid end to end, are cut into one
+//    contiguous range per wave.  No wave waits on a long segment while
+//    others idle, and a segment is split only where a range ends.  Ranges
+//    are weighted per XCD (workgroups are dealt round-robin to the 8 XCDs):
+//    on MI355X the even-numbered XCDs stream about 10% faster than the odd
+//    ones, so by default they get 10% more tiles (pa_set_balance_weights).
+//    When the caller says blocks are reused across sequences
+//    (PA_DECODE_KV_REUSED) and the unit count is a multiple of 8, the split
+//    is instead done per XCD: 8 sub-problems, units u = x (mod 8) on waves
+//    w = x (mod 8), so each KV head's blocks stay in one XCD's L2.
+//
+// Every reduction order is fixed by logical token position, so results are
+// deterministic and independent of where the blocks sit physically.
 //
 // Softmax runs in base 2: logits are multiplied by scale * log2(e) and
 // exponentiated with v_exp_f32; the stored partition maxima are base-2.
@@ -153,6 +168,19 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// K/V loads.  Streaming (NT): each block is read once in the call, so the
+// loads carry the non-temporal hint and do not displace other lines; on
+// MI355X this raises random 4 KiB gathers from ~6.0 to ~6.7 TB/s.  Reused
+// (!NT): blocks shared by several sequences are re-read, so they are loaded
+// normally and can hit in L2.
+template <typename V, bool NT>
+__device__ __forceinline__ V load_kv(const void *ptr) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const V *>(ptr));
+  else
+    return *reinterpret_cast<const V *>(ptr);
+}
+
 // ---- work decomposition ----------------------------------------------------
 
 struct Params {
@@ -162,71 +190,193 @@ struct Params {
   const char *value_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  float *ws_max, *ws_sum, *ws_acc;
+  float *ws_max, *ws_sum, *ws_acc;   // partial rows: [piece * gu + head in unit]
+  int32_t *seg_units;                // balanced: per segment, first and last owning wave
   int64_t num_blocks;
   int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, max_context_len;
-  int partition_size, num_partitions, units, group, head_tiles;
+  int partition_size;   // > 0 fixed partitions, 0 whole segments, < 0 balanced
+  int num_partitions;   // fixed mode: partitions of the longest sequence
+  int units;            // head units per sequence
+  int group;            // G = Hq / Hkv
+  int head_tiles;       // MFMA: 16-head tiles per KV head (1 for VALU)
+  int gu;               // partial rows per piece: heads a unit can hold
+  int waves;            // balanced mode: number of waves in the grid
+  int xsplit;           // balanced mode: sub-problems (1, or 8 = one per XCD)
+  int64_t id_stride;    // balanced mode: piece ids per sub-problem
+  int xcd_prefix[9];    // balanced mode: prefix sums of the 8 per-XCD weights
   float scale_log2e;
 };
 
-// Linear workgroup id -> (unit, sequence, partition).  The head unit varies
-// fastest: consecutive workgroups go round-robin to the 8 XCDs, so when the
-// unit count is a multiple of 8 every workgroup of one head unit lands on
-// the same XCD and shares its L2 (what the shared-prefix workload reuses).
-struct Work {
-  int unit, seq, part;
-  int t0, t1;     // token range [t0, t1) of this partition
-  int nparts;     // partitions of this sequence
-  bool active;    // false: nothing to do (partition past the end)
-};
-
-__device__ __forceinline__ Work decode_work(const Params &p) {
-  Work w;
-  int id = (int)blockIdx.x;
-  w.unit = id % p.units;
-  id /= p.units;
-  w.seq = id % p.num_seqs;
-  w.part = id / p.num_seqs;
-  int L = p.context_lens[w.seq];
-  L = L < 0 ? 0 : (L > p.max_context_len ? p.max_context_len : L);
-  if (p.partition_size > 0) {
-    w.nparts = (L + p.partition_size - 1) / p.partition_size;
-    w.t0 = w.part * p.partition_size;
-    w.t1 = min(L, w.t0 + p.partition_size);
-  } else {
-    w.nparts = L > 0 ? 1 : 0;
-    w.t0 = 0;
-    w.t1 = L;
-  }
-  // Partition 0 of an empty sequence still runs, to write the zero row.
-  w.active = w.part < (w.nparts > 0 ? w.nparts : 1);
-  return w;
+__device__ __forceinline__ int seq_len(const Params &p, int i) {
+  const int L = p.context_lens[i];
+  return L < 0 ? 0 : (L > p.max_context_len ? p.max_context_len : L);
 }
 
-// Block-table reader: 64 entries per VGPR chunk, read back with readlane.
-// Entries outside [0, num_blocks) are replaced by block 0, so a corrupt
-// table can give a wrong row but never an out-of-bounds access.
+__device__ __forceinline__ int tiles_of(int L) { return (L + 15) >> 4; }
+
+// One contiguous tile range [t0/16, ceil(t1/16)) of segment (seq, unit).
+struct Piece {
+  int seq, unit;
+  int t0, t1;       // tokens [t0, t1), t0 a multiple of 16
+  bool whole;       // covers the whole segment: write the output row
+  int64_t id;       // partial rows id * gu + h when !whole
+};
+
+// Block-table reader over blocks [first, first + count) of one table row:
+// 64 entries per VGPR chunk, read back with readlane.  Blocks are read in
+// order, so the chunk after the current one is requested as soon as the
+// current one is entered.  Entries outside [0, num_blocks) are replaced by
+// block 0, so a corrupt table can give a wrong row but never an
+// out-of-bounds access.
 struct TableReader {
   const int32_t *row;
-  int first, count;   // blocks [first, first + count) of the row
-  int chunk = -1;
-  int vals = 0;
-  int64_t num_blocks;
+  int first, count;
+  int chunk, vals, vals_next;
 
-  __device__ __forceinline__ int phys(int blk) {  // blk: absolute logical block
+  __device__ __forceinline__ int fetch(int c) const {
+    const int idx = (c << 6) + (int)threadIdx.x;
+    return idx < count ? row[first + idx] : 0;
+  }
+
+  // Request the first two chunks (no wait: the values are used later).
+  __device__ __forceinline__ void start(const Params &p, const Piece &pc, int bs) {
+    row = p.block_tables + (int64_t)pc.seq * p.max_blocks_per_seq;
+    first = pc.t0 / bs;
+    count = (pc.t1 + bs - 1) / bs - first;
+    chunk = 0;
+    vals = fetch(0);
+    vals_next = count > 64 ? fetch(1) : 0;
+  }
+
+  __device__ __forceinline__ int phys(int blk, int64_t num_blocks) {  // absolute logical block
     const int rel = blk - first;
     const int c = rel >> 6;
     if (c != chunk) {
+      vals = c == chunk + 1 ? vals_next : fetch(c);
       chunk = c;
-      const int idx = (c << 6) + (int)threadIdx.x;
-      vals = idx < count ? row[first + idx] : 0;
+      vals_next = ((c + 1) << 6) < count ? fetch(c + 1) : 0;
     }
-    int b = __builtin_amdgcn_readlane(vals, rel & 63);
+    const int b = __builtin_amdgcn_readlane(vals, rel & 63);
     return (unsigned)b < (unsigned long long)num_blocks ? b : 0;
   }
 };
 
-// ---- VALU kernel (MHA, or fp32 KV) ----------------------------------------
+// Context lengths of sequences [base, base + 64) in one VGPR, read back with
+// readlane; clamped like seq_len().
+struct LenWindow {
+  int base, vals;
+  __device__ __forceinline__ void load(const Params &p, int b) {
+    base = b;
+    const int i = b + (int)threadIdx.x;
+    vals = i < p.num_seqs ? seq_len(p, i) : 0;
+  }
+  __device__ __forceinline__ int get(const Params &p, int seq) {
+    if (seq - base >= 64 || seq < base) load(p, seq);
+    return __builtin_amdgcn_readlane(vals, seq - base);
+  }
+};
+
+#ifdef PA_WAVES_PER_EU
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_OCCUPANCY
+#endif
+
+// ---- the streaming driver ----------------------------------------------------
+//
+// A wave walks its pieces as one continuous stream of tiles, two tile
+// buffers deep: while one tile is computed the next one is in flight.  The
+// loader steps into the next piece as soon as the current one is fully
+// requested, so the first tiles of a piece are in flight while the last
+// tile of the previous one is computed.  One piece further on (the peeked
+// piece) has its first table chunk requested early, so stepping in never
+// waits on a table read.  With two buffers the loader is never more than one
+// piece ahead of the compute side: it holds that piece's query registers
+// until the compute side reaches it.
+//
+// Body provides Tile, QRaw (query registers as loaded), QReady (as used),
+// Acc (running max / sum / output) and: kBlockSize, head_offset, load_q,
+// ready_q, load_tile, init, compute, finish.
+
+template <class Body, class Gen>
+__device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (&p_lds)[2][16]) {
+  using Tile = typename Body::Tile;
+  using QRaw = typename Body::QRaw;
+  using QReady = typename Body::QReady;
+  using Acc = typename Body::Acc;
+  constexpr int BS = Body::kBlockSize;
+
+  Piece cp;                       // piece being computed
+  if (!gen.next(cp)) return;
+  Piece lp = cp;                  // piece being loaded
+  Piece pk;                       // peeked piece after lp (valid if has_pk)
+  bool has_pk = gen.next(pk);
+  TableReader tab, tab_pk;
+  tab.start(p, lp, BS);
+  if (has_pk) tab_pk.start(p, pk, BS);
+  QRaw qraw, qraw_next;
+  Body::load_q(p, cp, qraw);
+  QReady q;
+  int64_t head_off = Body::head_offset(p, lp.unit);
+  int lk = lp.t0 >> 4, lk1 = (lp.t1 + 15) >> 4;   // loader tile cursor
+  int ck = cp.t0 >> 4, ck1 = (cp.t1 + 15) >> 4;   // compute tile cursor
+  bool ahead = false;             // lp is the piece after cp
+  Acc acc;
+  Body::init(acc);
+
+  // Request the next tile of the stream into tl; false when none is left.
+  auto load_next = [&](Tile &tl) -> bool {
+    if (lk >= lk1) {
+      if (!has_pk) return false;
+      // Step into the peeked piece (its first table chunk is already
+      // requested) and request its query.
+      lp = pk;
+      tab = tab_pk;
+      head_off = Body::head_offset(p, lp.unit);
+      lk = lp.t0 >> 4;
+      lk1 = (lp.t1 + 15) >> 4;
+      Body::load_q(p, lp, qraw_next);
+      ahead = true;
+      has_pk = gen.next(pk);
+      if (has_pk) tab_pk.start(p, pk, BS);
+    }
+    Body::load_tile(p, tab, head_off, lk, tl);
+    ++lk;
+    return true;
+  };
+
+  // Compute one tile; at the end of a piece write its result and move to
+  // the next.  False when the last piece is done.  When cp ends, the loader
+  // has already tried to step past it (every tile of cp was requested at
+  // least one load earlier), so `ahead` tells whether a next piece exists.
+  auto consume = [&](Tile &tl) -> bool {
+    Body::compute(p, cp, q, acc, tl, ck, p_lds);
+    if (++ck < ck1) return true;
+    Body::finish(p, cp, acc);
+    if (!ahead) return false;
+    cp = lp;
+    Body::ready_q(p, cp, qraw_next, q);
+    ahead = false;
+    ck = cp.t0 >> 4;
+    ck1 = (cp.t1 + 15) >> 4;
+    Body::init(acc);
+    return true;
+  };
+
+  Tile b0, b1;
+  bool h0 = load_next(b0);
+  bool h1 = load_next(b1);
+  Body::ready_q(p, cp, qraw, q);   // after the first tiles are requested
+  while (h0) {
+    if (!consume(b0)) return;
+    h0 = load_next(b0);
+    if (!h1) return;
+    if (!consume(b1)) return;
+    h1 = load_next(b1);
+  }
+}
+
+// ---- VALU body (MHA, or fp32 KV) --------------------------------------------
 //
 // Lane l = 16*g + t.  Keys: for each tile, lane l loads the 16-byte key
 // chunks c = 4j + g (j < KJ) of token t; dot products are summed over the
@@ -235,113 +385,112 @@ struct TableReader {
 // loads 16-byte row segments (rows j*RPI + l/LPR, tokens X*(l%LPR)..+X) and
 // reads those tokens' probabilities from LDS.
 
-#ifdef PA_WAVES_PER_EU
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
-#else
-#define PA_OCCUPANCY
-#endif
-
-template <typename KV, int D, int BS, typename OUT>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_valu(Params p) {
-  constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
-  constexpr int KJ = D / X / 4;             // key chunks per lane per tile
-  constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
-  constexpr int RPI = 64 / LPR;             // value rows per load
-  constexpr int VJ = D / RPI;               // value loads per lane per tile
-  constexpr int TPB = BS / 16;              // tiles per block
+template <typename KV, int D, int BS, typename OUT, bool NT>
+struct ValuBody {
+  static constexpr int kBlockSize = BS;
+  static constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
+  static constexpr int KJ = D / X / 4;             // key chunks per lane per tile
+  static constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
+  static constexpr int RPI = 64 / LPR;             // value rows per load
+  static constexpr int VJ = D / RPI;               // value loads per lane per tile
+  static constexpr int TPB = BS / 16;              // tiles per block
   static_assert(KJ >= 1 && VJ >= 1, "unsupported shape");
-
-  const Work w = decode_work(p);
-  if (!w.active) return;
-  const int lane = (int)threadIdx.x;
-  const int t = lane & 15, g = lane >> 4;
-  const int qh = w.unit;
-  const int kvh = qh / p.group;
-  OUT *out = static_cast<OUT *>(p.out) + ((int64_t)w.seq * p.num_q_heads + qh) * D;
-
-  if (w.t1 <= w.t0) {  // empty sequence: zero row
-    for (int d = lane; d < D; d += 64) store_out<OUT>(out + d, 0.f);
-    return;
-  }
-
-  // Query chunks of this lane, pre-scaled into the base-2 logit domain.
-  float q[KJ][X];
-  {
-    const KV *qp = static_cast<const KV *>(p.query) + ((int64_t)w.seq * p.num_q_heads + qh) * D;
-#pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      const u32x4 c = *reinterpret_cast<const u32x4 *>(qp + (4 * j + g) * X);
-#pragma unroll
-      for (int e = 0; e < X; ++e) q[j][e] = elem<KV>(c, e) * p.scale_log2e;
-    }
-  }
-
-  const int64_t chunk_elems = (int64_t)D * BS;
-  const int64_t head_off = (int64_t)kvh * chunk_elems;
-  const int64_t block_stride = (int64_t)p.num_kv_heads * chunk_elems;
-  // Per-lane element offsets inside a (block, head) chunk, tile 0.
-  int koff[KJ], voff[VJ];
-#pragma unroll
-  for (int j = 0; j < KJ; ++j) koff[j] = ((4 * j + g) * BS + t) * X;
-  const int vrow = lane / LPR, vpiece = lane % LPR;
-#pragma unroll
-  for (int j = 0; j < VJ; ++j) voff[j] = (j * RPI + vrow) * BS + vpiece * X;
-
-  TableReader tab{p.block_tables + (int64_t)w.seq * p.max_blocks_per_seq, w.t0 / BS,
-                  (w.t1 + BS - 1) / BS - w.t0 / BS};
-  tab.num_blocks = p.num_blocks;
 
   struct Tile {
     u32x4 k[KJ];
     u32x4 v[VJ];
   };
-  auto load = [&](Tile &tl, int kt) {
+  struct QRaw {
+    u32x4 c[KJ];
+  };
+  struct QReady {
+    float v[KJ][X];
+  };
+  struct Acc {
+    float m, lsum;
+    float o[VJ];
+  };
+
+  __device__ static void zero_rows(const Params &p, int seq, int unit) {
+    OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + unit) * D;
+    for (int d = (int)threadIdx.x; d < D; d += 64) store_out<OUT>(out + d, 0.f);
+  }
+
+  __device__ static int64_t head_offset(const Params &p, int unit) {
+    return (int64_t)(unit / p.group) * D * BS;
+  }
+
+  // The lane's key chunks c = 4j + g of query head `unit`.
+  __device__ static void load_q(const Params &p, const Piece &pc, QRaw &q) {
+    const int g = (int)threadIdx.x >> 4;
+    const KV *qp =
+        static_cast<const KV *>(p.query) + ((int64_t)pc.seq * p.num_q_heads + pc.unit) * D;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) q.c[j] = *reinterpret_cast<const u32x4 *>(qp + (4 * j + g) * X);
+  }
+
+  // Widen and pre-scale into the base-2 logit domain.
+  __device__ static void ready_q(const Params &p, const Piece &, const QRaw &raw, QReady &q) {
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+#pragma unroll
+      for (int e = 0; e < X; ++e) q.v[j][e] = elem<KV>(raw.c[j], e) * p.scale_log2e;
+  }
+
+  __device__ static void load_tile(const Params &p, TableReader &tab, int64_t head_off, int kt,
+                                   Tile &tl) {
+    const int lane = (int)threadIdx.x;
+    const int t = lane & 15, g = lane >> 4;
     const int blk = kt / TPB, sub = kt % TPB;
-    const int64_t base = (int64_t)tab.phys(blk) * block_stride + head_off;
+    const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
     // Tile `sub` of a block: keys start 16 tokens * X further into each
     // [Bs][X] slab, values 16 tokens further into each [Bs] row.
     const KV *kb = reinterpret_cast<const KV *>(p.key_cache) + base + sub * 16 * X;
     const KV *vb = reinterpret_cast<const KV *>(p.value_cache) + base + sub * 16;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) tl.k[j] = *reinterpret_cast<const u32x4 *>(kb + koff[j]);
+    for (int j = 0; j < KJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + t) * X);
 #pragma unroll
-    for (int j = 0; j < VJ; ++j) tl.v[j] = *reinterpret_cast<const u32x4 *>(vb + voff[j]);
-  };
+    for (int j = 0; j < VJ; ++j)
+      tl.v[j] = load_kv<u32x4, NT>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X);
+  }
 
-  __shared__ float p_lds[2][16];
-  float m = -INFINITY, lsum = 0.f;
-  float o[VJ];
+  __device__ static void init(Acc &a) {
+    a.m = -INFINITY;
+    a.lsum = 0.f;
 #pragma unroll
-  for (int j = 0; j < VJ; ++j) o[j] = 0.f;
+    for (int j = 0; j < VJ; ++j) a.o[j] = 0.f;
+  }
 
-  auto compute = [&](Tile &tl, int kt) {
+  __device__ static void compute(const Params &, const Piece &pc, const QReady &q, Acc &a,
+                                 Tile &tl, int kt, float (&p_lds)[2][16]) {
+    const int lane = (int)threadIdx.x;
+    const int t = lane & 15, vpiece = lane % LPR;
     float dot = 0.f;
 #pragma unroll
     for (int j = 0; j < KJ; ++j)
 #pragma unroll
-      for (int e = 0; e < X; ++e) dot = fmaf(q[j][e], elem<KV>(tl.k[j], e), dot);
+      for (int e = 0; e < X; ++e) dot = fmaf(q.v[j][e], elem<KV>(tl.k[j], e), dot);
     dot += xor16(dot);
     dot += xor32(dot);
-    const int pos = kt * 16 + t;
-    const float s = pos < w.t1 ? dot : -INFINITY;
-    const float mnew = fmaxf(m, row16_max(s));
-    const float alpha = fast_exp2(m - mnew);
-    const float pr = fast_exp2(s - mnew);
-    lsum = lsum * alpha + pr;
-    if (mnew > m) {  // uniform: every row holds the same 16 logits
+    const float sc = kt * 16 + t < pc.t1 ? dot : -INFINITY;
+    const float mnew = fmaxf(a.m, row16_max(sc));
+    const float alpha = fast_exp2(a.m - mnew);
+    const float pr = fast_exp2(sc - mnew);
+    a.lsum = a.lsum * alpha + pr;
+    if (mnew > a.m) {  // uniform: every row holds the same 16 logits
 #pragma unroll
-      for (int j = 0; j < VJ; ++j) o[j] *= alpha;
+      for (int j = 0; j < VJ; ++j) a.o[j] *= alpha;
     }
-    m = mnew;
+    a.m = mnew;
     const int buf = kt & 1;
     if (lane < 16) p_lds[buf][t] = pr;
     __syncthreads();
-    if (kt * 16 + 16 > w.t1) {  // ragged last tile: unwritten slots may hold NaN
+    if (kt * 16 + 16 > pc.t1) {  // ragged last tile: unwritten slots may hold NaN
 #pragma unroll
       for (int j = 0; j < VJ; ++j)
 #pragma unroll
         for (int e = 0; e < X; ++e)
-          if (kt * 16 + vpiece * X + e >= w.t1) tl.v[j] = zero_elem<KV>(tl.v[j], e);
+          if (kt * 16 + vpiece * X + e >= pc.t1) tl.v[j] = zero_elem<KV>(tl.v[j], e);
     }
     float pv[X];
 #pragma unroll
@@ -349,48 +498,40 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_valu(Params p) {
 #pragma unroll
     for (int j = 0; j < VJ; ++j)
 #pragma unroll
-      for (int e = 0; e < X; ++e) o[j] = fmaf(pv[e], elem<KV>(tl.v[j], e), o[j]);
-  };
+      for (int e = 0; e < X; ++e) a.o[j] = fmaf(pv[e], elem<KV>(tl.v[j], e), a.o[j]);
+  }
 
-  const int k0 = w.t0 / 16, k1 = (w.t1 + 15) / 16;
-  Tile buf[kPrefetch];
+  // Combine the sum over the 16 token lanes and each row over its LPR lanes,
+  // then write the output row or the partial.
+  __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
+    const int lane = (int)threadIdx.x;
+    const int vrow = lane / LPR;
+    const float ltot = row16_sum(a.lsum);
 #pragma unroll
-  for (int s = 0; s < kPrefetch; ++s)
-    if (k0 + s < k1) load(buf[s], k0 + s);
-  for (int kt = k0; kt < k1; kt += kPrefetch) {
+    for (int j = 0; j < VJ; ++j) {
+      a.o[j] += dpp<kQuadXor1>(a.o[j]);
+      if (LPR == 4) a.o[j] += dpp<kQuadXor2>(a.o[j]);
+    }
+    if (lane % LPR == 0) {
+      if (pc.whole) {
+        OUT *out = static_cast<OUT *>(p.out) + ((int64_t)pc.seq * p.num_q_heads + pc.unit) * D;
+        const float inv = 1.f / ltot;
 #pragma unroll
-    for (int s = 0; s < kPrefetch; ++s) {
-      if (kt + s < k1) {
-        compute(buf[s], kt + s);
-        if (kt + s + kPrefetch < k1) load(buf[s], kt + s + kPrefetch);
+        for (int j = 0; j < VJ; ++j) store_out<OUT>(out + j * RPI + vrow, a.o[j] * inv);
+      } else {
+        const int64_t row = pc.id * p.gu;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) p.ws_acc[row * D + j * RPI + vrow] = a.o[j];
+        if (lane == 0) {
+          p.ws_max[row] = a.m;
+          p.ws_sum[row] = ltot;
+        }
       }
     }
   }
+};
 
-  // Combine: the sum over the 16 token lanes, the rows over their LPR lanes.
-  const float ltot = row16_sum(lsum);
-#pragma unroll
-  for (int j = 0; j < VJ; ++j) {
-    o[j] += dpp<kQuadXor1>(o[j]);
-    if (LPR == 4) o[j] += dpp<kQuadXor2>(o[j]);
-  }
-  if (vpiece != 0) return;
-  if (w.nparts <= 1) {
-    const float inv = 1.f / ltot;
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) store_out<OUT>(out + j * RPI + vrow, o[j] * inv);
-  } else {
-    const int64_t slot = ((int64_t)w.seq * p.num_q_heads + qh) * p.num_partitions + w.part;
-#pragma unroll
-    for (int j = 0; j < VJ; ++j) p.ws_acc[slot * D + j * RPI + vrow] = o[j];
-    if (lane == 0) {
-      p.ws_max[slot] = m;
-      p.ws_sum[slot] = ltot;
-    }
-  }
-}
-
-// ---- MFMA kernel (bf16 KV, G >= 2) -----------------------------------------
+// ---- MFMA body (bf16 KV, G >= 2) ---------------------------------------------
 //
 // Lane l = 16*g + c.  Q.K^T as S^T[t][h] = sum_d K[t][d] Q[h][d] with
 // v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 features (lane: token c,
@@ -403,213 +544,472 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_valu(Params p) {
 // quantity (max, sum, rescale) therefore lives in lane%16 = head, and the
 // accumulators are rescaled by each lane's own factor.
 
-template <int D, int BS, typename OUT>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_mfma(Params p) {
-  constexpr int QJ = D / 32;   // 16x16x32 steps over the features
-  constexpr int VT = D / 16;   // 16-feature output tiles
-  constexpr int TPB = BS / 16;
-
-  const Work w = decode_work(p);
-  if (!w.active) return;
-  const int lane = (int)threadIdx.x;
-  const int c = lane & 15, g = lane >> 4;
-  const int kvh = w.unit / p.head_tiles;
-  const int h = (w.unit % p.head_tiles) * 16 + c;   // head within the group
-  const bool live_head = h < p.group;
-  const int qh = kvh * p.group + h;
-  OUT *out = static_cast<OUT *>(p.out) + ((int64_t)w.seq * p.num_q_heads + qh) * D;
-
-  if (w.t1 <= w.t0) {  // empty sequence: zero rows
-    if (live_head)
-#pragma unroll
-      for (int i = 0; i < VT; ++i) store_out4<OUT>(out + 16 * i + 4 * g, 0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-
-  u32x4 qreg[QJ];
-  {
-    const bf16_t *qp = static_cast<const bf16_t *>(p.query) +
-                       ((int64_t)w.seq * p.num_q_heads + (live_head ? qh : 0)) * D;
-#pragma unroll
-    for (int j = 0; j < QJ; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(qp + (4 * j + g) * 8);
-      qreg[j] = live_head ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  const int64_t chunk_elems = (int64_t)D * BS;
-  const int64_t head_off = (int64_t)kvh * chunk_elems;
-  const int64_t block_stride = (int64_t)p.num_kv_heads * chunk_elems;
-  int koff[QJ], voff[VT];
-#pragma unroll
-  for (int j = 0; j < QJ; ++j) koff[j] = ((4 * j + g) * BS + c) * 8;
-#pragma unroll
-  for (int i = 0; i < VT; ++i) voff[i] = (16 * i + c) * BS + 4 * g;
-
-  TableReader tab{p.block_tables + (int64_t)w.seq * p.max_blocks_per_seq, w.t0 / BS,
-                  (w.t1 + BS - 1) / BS - w.t0 / BS};
-  tab.num_blocks = p.num_blocks;
+template <int D, int BS, typename OUT, bool NT>
+struct MfmaBody {
+  static constexpr int kBlockSize = BS;
+  static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
+  static constexpr int VT = D / 16;   // 16-feature output tiles
+  static constexpr int TPB = BS / 16;
 
   struct Tile {
     u32x4 k[QJ];
     u32x2 v[VT];
   };
-  auto load = [&](Tile &tl, int kt) {
+  struct QRaw {
+    u32x4 c[QJ];
+  };
+  using QReady = QRaw;
+  struct Acc {
+    float m, lsum;
+    mfma_f32x4 o[VT];
+  };
+
+  // Head of the group this lane's column holds, and whether it exists.
+  __device__ static int group_head(const Params &p, int unit) {
+    return (unit % p.head_tiles) * 16 + ((int)threadIdx.x & 15);
+  }
+
+  __device__ static void zero_rows(const Params &p, int seq, int unit) {
+    const int g = (int)threadIdx.x >> 4;
+    const int h = group_head(p, unit);
+    if (h >= p.group) return;
+    OUT *out = static_cast<OUT *>(p.out) +
+               ((int64_t)seq * p.num_q_heads + (unit / p.head_tiles) * p.group + h) * D;
+#pragma unroll
+    for (int i = 0; i < VT; ++i) store_out4<OUT>(out + 16 * i + 4 * g, 0.f, 0.f, 0.f, 0.f);
+  }
+
+  __device__ static int64_t head_offset(const Params &p, int unit) {
+    return (int64_t)(unit / p.head_tiles) * D * BS;
+  }
+
+  __device__ static void load_q(const Params &p, const Piece &pc, QRaw &q) {
+    const int g = (int)threadIdx.x >> 4;
+    const int h = group_head(p, pc.unit);
+    const int qh = (pc.unit / p.head_tiles) * p.group + (h < p.group ? h : 0);
+    const bf16_t *qp = static_cast<const bf16_t *>(p.query) +
+                       ((int64_t)pc.seq * p.num_q_heads + qh) * D;
+#pragma unroll
+    for (int j = 0; j < QJ; ++j) q.c[j] = *reinterpret_cast<const u32x4 *>(qp + (4 * j + g) * 8);
+  }
+
+  // Columns past the group's last head (a group of G < 16, or the last tile
+  // of G > 16) hold a copy of a real head's query: every column runs through
+  // both products on its own, so they cost nothing but unused outputs,
+  // which finish() never stores.
+  __device__ static void ready_q(const Params &, const Piece &, const QRaw &raw, QReady &q) {
+    q = raw;
+  }
+
+  __device__ static void load_tile(const Params &p, TableReader &tab, int64_t head_off, int kt,
+                                   Tile &tl) {
+    const int lane = (int)threadIdx.x;
+    const int c = lane & 15, g = lane >> 4;
     const int blk = kt / TPB, sub = kt % TPB;
-    const int64_t base = (int64_t)tab.phys(blk) * block_stride + head_off;
+    const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
     const bf16_t *kb = reinterpret_cast<const bf16_t *>(p.key_cache) + base + sub * 16 * 8;
     const bf16_t *vb = reinterpret_cast<const bf16_t *>(p.value_cache) + base + sub * 16;
 #pragma unroll
-    for (int j = 0; j < QJ; ++j) tl.k[j] = *reinterpret_cast<const u32x4 *>(kb + koff[j]);
+    for (int j = 0; j < QJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + c) * 8);
 #pragma unroll
-    for (int i = 0; i < VT; ++i) tl.v[i] = *reinterpret_cast<const u32x2 *>(vb + voff[i]);
-  };
+    for (int i = 0; i < VT; ++i) tl.v[i] = load_kv<u32x2, NT>(vb + (16 * i + c) * BS + 4 * g);
+  }
 
-  float m = -INFINITY, lsum = 0.f;
-  mfma_f32x4 acc[VT];
+  __device__ static void init(Acc &a) {
+    a.m = -INFINITY;
+    a.lsum = 0.f;
 #pragma unroll
-  for (int i = 0; i < VT; ++i) acc[i] = mfma_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < VT; ++i) a.o[i] = mfma_f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  auto compute = [&](Tile &tl, int kt) {
+  __device__ static void compute(const Params &p, const Piece &pc, const QReady &q, Acc &a,
+                                 Tile &tl, int kt, float (&)[2][16]) {
+    const int g = (int)threadIdx.x >> 4;
     mfma_f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < QJ; ++j)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfma_bf16x8, tl.k[j]),
-                                                  __builtin_bit_cast(mfma_bf16x8, qreg[j]), s,
-                                                  0, 0, 0);
+                                                  __builtin_bit_cast(mfma_bf16x8, q.c[j]), s, 0,
+                                                  0, 0);
     const int pos0 = kt * 16 + 4 * g;
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = pos0 + r < w.t1 ? s[r] * p.scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[r] = pos0 + r < pc.t1 ? s[r] * p.scale_log2e : -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    const float mnew = fmaxf(a.m, mx);
+    const float alpha = fast_exp2(a.m - mnew);
+    a.m = mnew;
     const unsigned p01 = pack_bf16x2(fast_exp2(sc[0] - mnew), fast_exp2(sc[1] - mnew));
     const unsigned p23 = pack_bf16x2(fast_exp2(sc[2] - mnew), fast_exp2(sc[3] - mnew));
     // The normaliser sums the same rounded probabilities the product uses.
-    lsum = lsum * alpha + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
-                           (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+    a.lsum = a.lsum * alpha + ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                               (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // some head's max moved
 #pragma unroll
-      for (int i = 0; i < VT; ++i) acc[i] *= alpha;
+      for (int i = 0; i < VT; ++i) a.o[i] *= alpha;
     }
-    if (kt * 16 + 16 > w.t1) {  // ragged last tile: unwritten slots may hold NaN
+    if (kt * 16 + 16 > pc.t1) {  // ragged last tile: unwritten slots may hold NaN
 #pragma unroll
       for (int i = 0; i < VT; ++i) {
-        if (pos0 + 0 >= w.t1) tl.v[i][0] &= 0xffff0000u;
-        if (pos0 + 1 >= w.t1) tl.v[i][0] &= 0x0000ffffu;
-        if (pos0 + 2 >= w.t1) tl.v[i][1] &= 0xffff0000u;
-        if (pos0 + 3 >= w.t1) tl.v[i][1] &= 0x0000ffffu;
+        if (pos0 + 0 >= pc.t1) tl.v[i][0] &= 0xffff0000u;
+        if (pos0 + 1 >= pc.t1) tl.v[i][0] &= 0x0000ffffu;
+        if (pos0 + 2 >= pc.t1) tl.v[i][1] &= 0xffff0000u;
+        if (pos0 + 3 >= pc.t1) tl.v[i][1] &= 0x0000ffffu;
       }
     }
     const mfma_i16x4 pb = __builtin_bit_cast(mfma_i16x4, u32x2{p01, p23});
 #pragma unroll
     for (int i = 0; i < VT; ++i)
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_i16x4, tl.v[i]),
-                                                         pb, acc[i], 0, 0, 0);
-  };
+      a.o[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_i16x4, tl.v[i]),
+                                                         pb, a.o[i], 0, 0, 0);
+  }
 
-  const int k0 = w.t0 / 16, k1 = (w.t1 + 15) / 16;
-  Tile buf[kPrefetch];
+  __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
+    const int g = (int)threadIdx.x >> 4, hh = (int)threadIdx.x & 15;
+    float ltot = a.lsum + xor16(a.lsum);
+    ltot += xor32(ltot);
+    const int h = group_head(p, pc.unit);
+    if (h >= p.group) return;
+    const int qh = (pc.unit / p.head_tiles) * p.group + h;
+    if (pc.whole) {
+      OUT *out = static_cast<OUT *>(p.out) + ((int64_t)pc.seq * p.num_q_heads + qh) * D;
+      const float inv = 1.f / ltot;
 #pragma unroll
-  for (int s = 0; s < kPrefetch; ++s)
-    if (k0 + s < k1) load(buf[s], k0 + s);
-  for (int kt = k0; kt < k1; kt += kPrefetch) {
+      for (int i = 0; i < VT; ++i)
+        store_out4<OUT>(out + 16 * i + 4 * g, a.o[i][0] * inv, a.o[i][1] * inv, a.o[i][2] * inv,
+                        a.o[i][3] * inv);
+    } else {
+      const int64_t row = pc.id * p.gu + hh;
 #pragma unroll
-    for (int s = 0; s < kPrefetch; ++s) {
-      if (kt + s < k1) {
-        compute(buf[s], kt + s);
-        if (kt + s + kPrefetch < k1) load(buf[s], kt + s + kPrefetch);
+      for (int i = 0; i < VT; ++i)
+        *reinterpret_cast<f32x4 *>(p.ws_acc + row * D + 16 * i + 4 * g) =
+            f32x4{a.o[i][0], a.o[i][1], a.o[i][2], a.o[i][3]};
+      if (g == 0) {
+        p.ws_max[row] = a.m;
+        p.ws_sum[row] = ltot;
       }
     }
   }
+};
 
-  float ltot = lsum + xor16(lsum);
-  ltot += xor32(ltot);
-  if (!live_head) return;
-  if (w.nparts <= 1) {
-    const float inv = 1.f / ltot;
-#pragma unroll
-    for (int i = 0; i < VT; ++i)
-      store_out4<OUT>(out + 16 * i + 4 * g, acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv,
-                      acc[i][3] * inv);
-  } else {
-    const int64_t slot = ((int64_t)w.seq * p.num_q_heads + qh) * p.num_partitions + w.part;
-#pragma unroll
-    for (int i = 0; i < VT; ++i)
-      *reinterpret_cast<f32x4 *>(p.ws_acc + slot * D + 16 * i + 4 * g) =
-          f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-    if (g == 0) {
-      p.ws_max[slot] = m;
-      p.ws_sum[slot] = ltot;
-    }
+// ---- grid strategies ---------------------------------------------------------
+
+// Fixed partitions: workgroup id -> (unit, sequence, partition), the unit
+// varying fastest.  Consecutive workgroups go round-robin to the 8 XCDs, so
+// when the unit count is a multiple of 8 every workgroup of one head unit
+// lands on the same XCD and shares its L2 (what shared prefixes reuse).
+struct OnePiece {
+  Piece pc;
+  bool given;
+  __device__ bool next(Piece &out) {
+    if (given) return false;
+    given = true;
+    out = pc;
+    return true;
   }
+};
+
+template <class Body>
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
+  __shared__ float p_lds[2][16];
+  int id = (int)blockIdx.x;
+  const int unit = id % p.units;
+  id /= p.units;
+  const int seq = id % p.num_seqs;
+  const int part = id / p.num_seqs;
+  const int L = seq_len(p, seq);
+  int nparts, t0, t1;
+  if (p.partition_size > 0) {
+    nparts = (L + p.partition_size - 1) / p.partition_size;
+    t0 = part * p.partition_size;
+    t1 = min(L, t0 + p.partition_size);
+  } else {
+    nparts = L > 0 ? 1 : 0;
+    t0 = 0;
+    t1 = L;
+  }
+  if (L == 0) {   // the zero row, written once
+    if (part == 0) Body::zero_rows(p, seq, unit);
+    return;
+  }
+  if (part >= nparts) return;
+  OnePiece gen{Piece{seq, unit, t0, t1, nparts == 1,
+                     ((int64_t)seq * p.units + unit) * p.num_partitions + part},
+               false};
+  stream_pieces<Body>(p, gen, p_lds);
 }
 
-// ---- log-sum-exp merge of partitions ----------------------------------------
+// Sum over the wave (all lanes get it).
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = (int)threadIdx.x & 63;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// Tiles of one unit summed over all sequences: sum_i ceil(L_i / 16).
+__device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
+  int64_t tot = 0;
+  for (int c = 0; c < p.num_seqs; c += 64) {
+    const int i = c + ((int)threadIdx.x & 63);
+    tot += wave_sum(i < p.num_seqs ? tiles_of(seq_len(p, i)) : 0);
+  }
+  return tot;
+}
+
+// Two waves per SIMD at least: a single resident wave cannot keep enough
+// bytes in flight.
+#ifdef PA_WAVES_PER_EU
+#define PA_BALANCED_OCCUPANCY PA_OCCUPANCY
+#else
+#define PA_BALANCED_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
+#endif
+
+// Balanced split.  Sub-problem x (of xsplit) holds the head units
+// u = x + xsplit*k, k < Ux = units / xsplit, of every sequence, and the waves
+// w = x + xsplit*j, j < Wx = waves / xsplit.  Its segments (seq, k), laid end
+// to end in that order, hold T = Ux * sum_i tiles_i tiles, cut into one
+// contiguous range per wave.  Ranges are weighted: workgroups are dealt
+// round-robin to the 8 XCDs, so wave j of a single sub-problem runs on XCD
+// j mod 8, and XCDs that stream faster get proportionally more tiles
+// (weights: one per XCD, prefix sums in Params::xcd_prefix).  Every range
+// is nonempty, so along the tile line the wave index j and the local
+// segment index s = seq * Ux + k both only grow: the piece of segment s in
+// wave j's range gets id x * id_stride + s + j, ids of distinct pieces
+// differ, and a segment's pieces have consecutive ids.  The wave producing
+// a segment's first (last) piece records j in seg_units[2*g] ([2*g+1]),
+// g = seq * units + u, for the merge.
+struct Split {
+  int64_t T, W;
+  bool weighted;
+  const Params *p;
+  __device__ Split(const Params &pp, int64_t unit_tiles) : p(&pp) {
+    const int64_t wx = pp.waves / pp.xsplit;
+    T = unit_tiles * (pp.units / pp.xsplit);
+    // A weighted range holds at least floor(T * weight / sum of weights)
+    // tiles: all are nonempty when T * min weight >= that sum.  Otherwise
+    // plain equal ranges over at most T waves.
+    int wmin = pp.xcd_prefix[1] - pp.xcd_prefix[0];
+    for (int i = 1; i < 8; ++i) wmin = min(wmin, pp.xcd_prefix[i + 1] - pp.xcd_prefix[i]);
+    weighted = pp.xsplit == 1 && T * wmin >= cum(wx);
+    W = weighted ? wx : (T < wx ? T : wx);
+  }
+  // Weighted waves before wave j: sum over v < j of weight[v mod 8].
+  __device__ int64_t cum(int64_t j) const {
+    return (j >> 3) * p->xcd_prefix[8] + p->xcd_prefix[j & 7];
+  }
+  __device__ int64_t begin(int64_t j) const {
+    return weighted ? T * cum(j) / cum(W) : T * j / W;
+  }
+};
+
+struct RangePieces {
+  const Params *p;
+  int x, ux, seq, k, a, L, n_seq;
+  int64_t unit, t, te, id_base;
+  LenWindow lens;
+
+  __device__ bool next(Piece &out) {
+    if (t >= te) return false;
+    const int len = (int)min((int64_t)(n_seq - a), te - t);
+    const int b = a + len;
+    const int u = x + p->xsplit * k;
+    const int64_t g = (int64_t)seq * p->units + u;
+    if (threadIdx.x == 0) {
+      if (a == 0) p->seg_units[2 * g] = (int32_t)unit;
+      if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
+    }
+    out = Piece{seq, u, a * 16, min(b * 16, L), a == 0 && b == n_seq,
+                id_base + (int64_t)seq * ux + k + unit};
+    t += len;
+    a = 0;
+    if (t < te && ++k == ux) {
+      k = 0;
+      do {
+        if (++seq >= p->num_seqs) {   // unreachable while t < te
+          t = te;
+          break;
+        }
+        L = lens.get(*p, seq);
+        n_seq = tiles_of(L);
+      } while (n_seq == 0);
+    }
+    return true;
+  }
+};
+
+template <class Body>
+__global__ __launch_bounds__(64) PA_BALANCED_OCCUPANCY void decode_balanced(Params p) {
+  __shared__ float p_lds[2][16];
+  const int lane = (int)threadIdx.x;
+  RangePieces gen;
+  gen.p = &p;
+  gen.x = (int)blockIdx.x % p.xsplit;
+  gen.unit = (int64_t)blockIdx.x / p.xsplit;
+  gen.ux = p.units / p.xsplit;
+  const Split sp(p, tiles_per_unit(p));
+  if (gen.unit >= sp.W) return;
+  gen.t = sp.begin(gen.unit);
+  gen.te = sp.begin(gen.unit + 1);
+  gen.id_base = (int64_t)gen.x * p.id_stride;
+  // Find the sequence holding tile t: the first whose cumulative tiles pass t.
+  gen.seq = -1;
+  int64_t seq_first = 0, base = 0;
+  for (int c = 0; c < p.num_seqs && gen.seq < 0; c += 64) {
+    const int i = c + lane;
+    const int n = i < p.num_seqs ? tiles_of(seq_len(p, i)) : 0;
+    const int incl = wave_incl_scan(n);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64((base + incl) * gen.ux > gen.t);
+    if (hit) {
+      const int l0 = (int)__builtin_ctzll(hit);
+      gen.seq = c + l0;
+      gen.n_seq = __builtin_amdgcn_readlane(n, l0);
+      seq_first = (base + __builtin_amdgcn_readlane(incl, l0) - gen.n_seq) * gen.ux;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (gen.seq < 0) return;   // unreachable while t < T
+  gen.lens.load(p, gen.seq);
+  gen.L = gen.lens.get(p, gen.seq);
+  gen.k = (int)((gen.t - seq_first) / gen.n_seq);
+  gen.a = (int)((gen.t - seq_first) % gen.n_seq);
+  stream_pieces<Body>(p, gen, p_lds);
+}
+
+// ---- log-sum-exp merge -------------------------------------------------------
 //
-// Per (sequence, query head) with n > 1 partitions holding base-2 maxima
-// m_p, sums l_p and unnormalised outputs o_p:
+// One wave per output row (sequence, unit, head in unit).  A row split into
+// pieces with base-2 maxima m_p, sums l_p and unnormalised outputs o_p gets
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// accumulated in partition order.
+// the maxima and sums reduced across lanes, the outputs accumulated in piece
+// order.  Rows of one piece were written whole by the main kernel; in
+// balanced mode this kernel also writes the zero rows of empty sequences.
+
+__device__ __forceinline__ float wave_max_f(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 
 template <int D, typename OUT>
-__global__ __launch_bounds__(64) void decode_reduce(Params p) {
-  const int qh = (int)blockIdx.x % p.num_q_heads;
-  const int seq = (int)blockIdx.x / p.num_q_heads;
-  int L = p.context_lens[seq];
-  L = L < 0 ? 0 : (L > p.max_context_len ? p.max_context_len : L);
-  const int n = (L + p.partition_size - 1) / p.partition_size;
-  if (n <= 1) return;
-  const int64_t base = ((int64_t)seq * p.num_q_heads + qh) * p.num_partitions;
+__global__ __launch_bounds__(64) void decode_merge(Params p) {
   const int lane = (int)threadIdx.x;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, p.ws_max[base + i]);
+  int r = (int)blockIdx.x;
+  const int hh = r % p.gu;
+  r /= p.gu;
+  const int unit = r % p.units;
+  const int seq = r / p.units;
+  int qh;
+  if (p.head_tiles == 1 && p.gu == 1) {
+    qh = unit;
+  } else {
+    const int h = (unit % p.head_tiles) * 16 + hh;
+    if (h >= p.group) return;
+    qh = (unit / p.head_tiles) * p.group + h;
+  }
   constexpr int R = D / 64;
+  OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + qh) * D;
+  const int L = seq_len(p, seq);
+  const bool balanced = p.partition_size < 0;
+  if (L == 0) {
+    if (balanced)
+#pragma unroll
+      for (int k = 0; k < R; ++k) store_out<OUT>(out + k * 64 + lane, 0.f);
+    return;
+  }
+  int64_t id0;
+  int n;
+  if (balanced) {
+    const int64_t g = (int64_t)seq * p.units + unit;
+    const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
+    const int x = unit % p.xsplit, ux = p.units / p.xsplit;
+    n = u1 - u0 + 1;
+    id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
+  } else {
+    n = p.partition_size > 0 ? (L + p.partition_size - 1) / p.partition_size : 1;
+    id0 = ((int64_t)seq * p.units + unit) * p.num_partitions;
+  }
+  if (n <= 1) return;
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.ws_max[(id0 + i) * p.gu + hh]);
+  M = wave_max_f(M);
+  float den = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    const int64_t row = (id0 + i) * p.gu + hh;
+    den += fast_exp2(p.ws_max[row] - M) * p.ws_sum[row];
+  }
+  den = wave_sum_f(den);
   float num[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) num[r] = 0.f;
-  float den = 0.f;
+  for (int k = 0; k < R; ++k) num[k] = 0.f;
+#pragma unroll 4
   for (int i = 0; i < n; ++i) {
-    const float wgt = fast_exp2(p.ws_max[base + i] - M);
-    den = fmaf(wgt, p.ws_sum[base + i], den);
-    const float *acc = p.ws_acc + (base + i) * D;
+    const int64_t row = (id0 + i) * p.gu + hh;
+    const float wgt = fast_exp2(p.ws_max[row] - M);
+    const float *acc = p.ws_acc + row * D;
 #pragma unroll
-    for (int r = 0; r < R; ++r) num[r] = fmaf(wgt, acc[r * 64 + lane], num[r]);
+    for (int k = 0; k < R; ++k) num[k] = fmaf(wgt, acc[k * 64 + lane], num[k]);
   }
-  OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + qh) * D;
   const float inv = 1.f / den;
 #pragma unroll
-  for (int r = 0; r < R; ++r) store_out<OUT>(out + r * 64 + lane, num[r] * inv);
+  for (int k = 0; k < R; ++k) store_out<OUT>(out + k * 64 + lane, num[k] * inv);
 }
 
-// ---- dispatch ---------------------------------------------------------------
+// ---- dispatch ----------------------------------------------------------------
 
-template <typename KV, int D, int BS, typename OUT>
-hipError_t launch_valu(const Params &p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_valu<KV, D, BS, OUT>), dim3(grid), dim3(64), 0, st, p);
+// Waves of `kernel` the device holds at once (64-thread workgroups).
+int resident_waves(const void *kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+template <class Body, typename OUT>
+hipError_t launch_body(const DecodeArgs &a, Params &p, hipStream_t st) {
+  if (p.partition_size < 0) {
+    const void *k = reinterpret_cast<const void *>(&decode_balanced<Body>);
+    const BalancedPlan plan = balanced_plan(a, p.units, resident_waves(k));
+    if (plan.waves <= 0) return hipErrorInvalidDevice;
+    p.waves = plan.waves;
+    p.xsplit = plan.xsplit;
+    p.id_stride = plan.id_stride;
+    p.xcd_prefix[0] = 0;
+    for (int i = 0; i < 8; ++i) p.xcd_prefix[i + 1] = p.xcd_prefix[i] + a.xcd_weights[i];
+    hipLaunchKernelGGL((decode_balanced<Body>), dim3(plan.waves), dim3(64), 0, st, p);
+  } else {
+    const int64_t grid = (int64_t)p.units * a.num_seqs * p.num_partitions;
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_fixed<Body>), dim3((unsigned)grid), dim3(64), 0, st, p);
+  }
   return hipGetLastError();
 }
 
-template <int D, int BS, typename OUT>
-hipError_t launch_mfma(const Params &p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_mfma<D, BS, OUT>), dim3(grid), dim3(64), 0, st, p);
-  return hipGetLastError();
-}
-
-template <typename OUT>
-hipError_t dispatch_out(const DecodeArgs &a, const Params &p, bool use_mfma, int grid,
-                        hipStream_t st) {
+template <typename OUT, bool NT>
+hipError_t dispatch_out(const DecodeArgs &a, Params &p, bool use_mfma, hipStream_t st) {
   const bool bf = a.kv_dtype == PA_BF16;
   const int D = a.head_dim, BS = a.block_size;
 #define PA_CASE(d, bs)                                                              \
   if (D == d && BS == bs) {                                                         \
-    if (use_mfma) return launch_mfma<d, bs, OUT>(p, grid, st);                      \
-    return bf ? launch_valu<bf16_t, d, bs, OUT>(p, grid, st)                        \
-              : launch_valu<float, d, bs, OUT>(p, grid, st);                        \
+    if (use_mfma) return launch_body<MfmaBody<d, bs, OUT, NT>, OUT>(a, p, st);      \
+    return bf ? launch_body<ValuBody<bf16_t, d, bs, OUT, NT>, OUT>(a, p, st)        \
+              : launch_body<ValuBody<float, d, bs, OUT, NT>, OUT>(a, p, st);        \
   }
   PA_CASE(64, 16)
   PA_CASE(64, 32)
@@ -620,21 +1020,52 @@ hipError_t dispatch_out(const DecodeArgs &a, const Params &p, bool use_mfma, int
 }
 
 template <typename OUT>
-hipError_t launch_reduce(const DecodeArgs &a, const Params &p, hipStream_t st) {
-  const int grid = a.num_seqs * a.num_q_heads;
+hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
+  const int64_t rows = (int64_t)a.num_seqs * p.units * p.gu;
+  if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_reduce<64, OUT>), dim3(grid), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge<64, OUT>), dim3((unsigned)rows), dim3(64), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_reduce<128, OUT>), dim3(grid), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge<128, OUT>), dim3((unsigned)rows), dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident) {
+  // Reused blocks: split by XCD so that each KV head's blocks stay in one
+  // L2.  Streaming: one weighted split over all XCDs.
+  BalancedPlan pl;
+  int w = resident < a.max_waves ? resident : a.max_waves;
+  // No more waves than give each at least kMinTiles tiles of the largest
+  // possible problem: small calls are not shattered into one-tile pieces.
+  constexpr int64_t kMinTiles = 8;
+  const int64_t tiles_max = (a.max_context_len + 15) / 16;
+  const int64_t t_upper = (int64_t)units * a.num_seqs * tiles_max;
+  const int64_t cap = (t_upper + kMinTiles - 1) / kMinTiles;
+  if (cap < w) w = cap > 0 ? (int)cap : 1;
+  pl.xsplit = ((a.flags & PA_DECODE_KV_REUSED) && units % 8 == 0 && w >= 64) ? 8 : 1;
+  if (w >= 8) w -= w % 8;   // whole rounds of the 8 XCDs
+  w -= w % pl.xsplit;
+  pl.waves = w;
+  pl.id_stride = (int64_t)a.num_seqs * (units / pl.xsplit) + w / pl.xsplit;
+  pl.rows = (size_t)pl.xsplit * pl.id_stride;
+  return pl;
+}
+
+HeadUnits head_units(int32_t num_q_heads, int32_t num_kv_heads, pa_dtype kv_dtype) {
+  const int G = num_q_heads / num_kv_heads;
+  HeadUnits u;
+  u.mfma = kv_dtype == PA_BF16 && G >= 2;
+  u.head_tiles = u.mfma ? (G + 15) / 16 : 1;
+  u.units = u.mfma ? num_kv_heads * u.head_tiles : num_q_heads;
+  u.gu = u.mfma ? (G < 16 ? G : 16) : 1;
+  return u;
+}
+
 int launch_decode(const DecodeArgs &a, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const bool use_mfma = a.kv_dtype == PA_BF16 && G >= 2;
+  const HeadUnits hu = head_units(a.num_q_heads, a.num_kv_heads, a.kv_dtype);
   Params p;
   p.out = a.out;
   p.query = a.query;
@@ -645,6 +1076,7 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.ws_max = a.ws_max;
   p.ws_sum = a.ws_sum;
   p.ws_acc = a.ws_acc;
+  p.seg_units = a.seg_units;
   p.num_blocks = a.num_blocks;
   p.num_seqs = a.num_seqs;
   p.num_q_heads = a.num_q_heads;
@@ -653,28 +1085,34 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.max_context_len = a.max_context_len;
   p.partition_size = a.partition_size;
   p.num_partitions = a.num_partitions;
-  p.group = G;
-  p.head_tiles = use_mfma ? (G + 15) / 16 : 1;
-  p.units = use_mfma ? a.num_kv_heads * p.head_tiles : a.num_q_heads;
+  p.units = hu.units;
+  p.group = a.num_q_heads / a.num_kv_heads;
+  p.head_tiles = hu.head_tiles;
+  p.gu = hu.gu;
+  p.waves = 0;
+  p.xsplit = 1;
+  p.id_stride = 0;
   p.scale_log2e = a.scale * kLog2e;
-  const int64_t grid64 = (int64_t)p.units * a.num_seqs * a.num_partitions;
-  if (grid64 <= 0) return (int)hipSuccess;   // unreachable: num_seqs > 0 is checked
-  if (grid64 > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-  const int grid = (int)grid64;
   hipError_t e;
   if (a.ev_before_main) {
     e = hipEventRecord(static_cast<hipEvent_t>(a.ev_before_main), st);
     if (e != hipSuccess) return (int)e;
   }
-  e = a.out_dtype == PA_BF16 ? dispatch_out<bf16_t>(a, p, use_mfma, grid, st)
-                             : dispatch_out<float>(a, p, use_mfma, grid, st);
+  const bool reused = (a.flags & PA_DECODE_KV_REUSED) != 0;
+  if (a.out_dtype == PA_BF16)
+    e = reused ? dispatch_out<bf16_t, false>(a, p, hu.mfma, st)
+               : dispatch_out<bf16_t, true>(a, p, hu.mfma, st);
+  else
+    e = reused ? dispatch_out<float, false>(a, p, hu.mfma, st)
+               : dispatch_out<float, true>(a, p, hu.mfma, st);
   if (e != hipSuccess) return (int)e;
   if (a.ev_after_main) {
     e = hipEventRecord(static_cast<hipEvent_t>(a.ev_after_main), st);
     if (e != hipSuccess) return (int)e;
   }
-  if (a.num_partitions <= 1) return (int)e;
-  e = a.out_dtype == PA_BF16 ? launch_reduce<bf16_t>(a, p, st) : launch_reduce<float>(a, p, st);
+  const bool merge = a.partition_size < 0 || a.num_partitions > 1;
+  if (!merge) return (int)hipSuccess;
+  e = a.out_dtype == PA_BF16 ? launch_merge<bf16_t>(a, p, st) : launch_merge<float>(a, p, st);
   return (int)e;
 }
 

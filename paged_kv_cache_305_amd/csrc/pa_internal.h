@@ -21,19 +21,45 @@ struct DecodeArgs {
   int64_t num_blocks;
   int32_t max_context_len;
   float scale;
-  int32_t partition_size;   // 0: one partition per sequence
-  int32_t num_partitions;   // partitions of the longest sequence (grid extent)
+  int32_t partition_size;   // > 0 fixed partitions, 0 whole segments, < 0 balanced
+  int32_t num_partitions;   // fixed mode: partitions of the longest sequence
+  int32_t max_waves;        // balanced mode: upper bound of the wave count
   pa_dtype kv_dtype, out_dtype;
-  float *ws_max, *ws_sum, *ws_acc;  // split-K partials, null when num_partitions <= 1
+  uint32_t flags;           // PA_DECODE_* bits
+  float *ws_max, *ws_sum, *ws_acc;  // split partials, null when every row is written whole
+  int32_t *seg_units;               // balanced mode: 2 ints per (sequence, head unit)
+  int32_t xcd_weights[8];           // balanced mode: relative tile share per XCD
   void *ev_before_main, *ev_after_main;  // optional hipEvent_t pair around the main kernel
 };
 
-// Workspace carve-up shared by the size query and the decode call.
-struct WorkspaceLayout {
-  size_t max_off, sum_off, acc_off, total;
+// How query heads are grouped into head units (one wave's worth of heads).
+struct HeadUnits {
+  bool mfma;       // bf16 KV with G >= 2: MFMA body, one KV head per unit
+  int head_tiles;  // 16-head tiles per KV head (MFMA), else 1
+  int units;       // head units per sequence
+  int gu;          // partial rows per piece: heads one unit holds
 };
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t num_partitions);
+HeadUnits head_units(int32_t num_q_heads, int32_t num_kv_heads, pa_dtype kv_dtype);
+
+// Balanced split: one contiguous, per-XCD weighted range of tiles per wave.
+struct BalancedPlan {
+  int waves, xsplit;
+  int64_t id_stride;   // piece ids per sub-problem
+  size_t rows;         // pieces in all sub-problems (partial rows = rows * gu)
+};
+// `resident`: waves the device holds at once for the kernel.
+BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident);
+
+// Current per-XCD weights (pa_set_balance_weights).
+void balance_weights(int32_t out[8]);
+
+// Workspace carve-up shared by the size query and the decode call: `rows`
+// partial rows, each a base-2 max, a sum and head_dim unnormalised outputs,
+// then `segments` pairs of int32 (balanced mode's first/last owning wave).
+struct WorkspaceLayout {
+  size_t rows, max_off, sum_off, acc_off, seg_off, total;
+};
+WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments);
 
 // Kernel launchers (pa_decode.hip, pa_cache.hip); they return hipError_t as int.
 int launch_decode(const DecodeArgs &a, void *stream);

@@ -40,6 +40,7 @@ class DecodeStep:
     max_context_len: int
     scale: float
     partition_size: int
+    kv_reused: bool = False
 
     @property
     def num_pairs(self) -> int:
@@ -62,7 +63,8 @@ class DecodeStep:
                                  num_kv_heads=self.num_kv_heads, block_size=self.block_size,
                                  max_context_len=self.max_context_len, scale=self.scale,
                                  partition_size=self.partition_size, workspace=self.workspace,
-                                 num_blocks=self.num_blocks, stream=stream)
+                                 num_blocks=self.num_blocks, kv_reused=self.kv_reused,
+                                 stream=stream)
 
     def run(self, stream=None):
         self.copy(stream)
@@ -82,8 +84,8 @@ def _finish(query, key_cache, value_cache, new_key, new_value, slots, pairs, tab
     t_lens = torch.as_tensor(np.ascontiguousarray(lens, dtype=np.int32)).to(dev)
     mcl = int(np.max(lens)) if len(lens) else 0
     out = torch.empty(query.shape, dtype=out_dtype or query.dtype, device=dev)
-    nbytes = B.paged_attention_workspace_bytes(query.shape[0], query.shape[1], head_dim, mcl,
-                                               partition_size)
+    nbytes = B.paged_attention_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
+                                               head_dim, mcl, partition_size, query.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
     return DecodeStep(query, key_cache, value_cache, new_key, new_value, t_slots, t_pairs, t_tab,
                       t_lens, out, ws, num_kv_heads, head_dim, block_size, num_blocks, mcl, scale,
@@ -141,5 +143,7 @@ def shared_prefix_step(plan, tensors, partition_size: int, out_dtype=None):
                    num_kv_heads=tensors["num_kv_heads"], head_dim=tensors["head_dim"],
                    block_size=plan.block_size, num_blocks=plan.num_blocks,
                    scale=tensors["scale"], partition_size=partition_size, out_dtype=out_dtype)
+    # The prompt's blocks are shared by every sequence: keep them in the caches.
+    step.kv_reused = True
     record = dict(slots=slots, pairs=pairs, tables=tables, lens=lens32, allocator=a)
     return step, record

@@ -15,7 +15,7 @@ def to_dev(a, dtype=None):
 
 
 def gpu_decode(pa, case, partition_size=0, out_dtype=None, tables=None, lens=None, query=None,
-               key_cache=None, value_cache=None, max_context_len=None):
+               key_cache=None, value_cache=None, max_context_len=None, kv_reused=False):
     q = case.query if query is None else query
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device="cuda")
     tab = to_dev(case.block_tables if tables is None else tables)
@@ -25,7 +25,8 @@ def gpu_decode(pa, case, partition_size=0, out_dtype=None, tables=None, lens=Non
         out, q, case.key_cache if key_cache is None else key_cache,
         case.value_cache if value_cache is None else value_cache, tab, ln,
         num_kv_heads=case.num_kv_heads, block_size=case.block_size, max_context_len=mcl,
-        scale=case.scale, partition_size=partition_size, num_blocks=case.num_blocks)
+        scale=case.scale, partition_size=partition_size, num_blocks=case.num_blocks,
+        kv_reused=kv_reused)
     torch.cuda.synchronize()
     return out
 

@@ -37,7 +37,7 @@ def _decode(lib, **kw):
              context_lens=NULL, num_seqs=1, num_q_heads=8, num_kv_heads=2, head_dim=128,
              block_size=16, max_blocks_per_seq=4, num_blocks=16, max_context_len=64,
              scale=0.1, partition_size=0, kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16,
-             workspace=NULL, workspace_bytes=0, stream=NULL)
+             flags=0, workspace=NULL, workspace_bytes=0, stream=NULL)
     a.update(kw)
     return lib.pa_paged_attention_decode(*a.values())
 
@@ -51,6 +51,7 @@ def _decode(lib, **kw):
     (dict(max_context_len=65), pa.PA_ERR_INVALID_ARG),
     (dict(partition_size=24), pa.PA_ERR_INVALID_ARG),
     (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(flags=2), pa.PA_ERR_INVALID_ARG),
     (dict(), pa.PA_ERR_INVALID_ARG),                        # null pointers
     (dict(out=16, query=32, key_cache=48, value_cache=64, block_tables=8, context_lens=8,
           partition_size=16), pa.PA_ERR_INVALID_ARG),     # workspace missing
@@ -70,13 +71,22 @@ def test_decode_with_no_sequences_is_a_no_op():
 
 def test_workspace_size():
     lib = pa.load()
-    assert pa.paged_attention_workspace_bytes(8, 32, 128, 32768, 0) == 0
-    assert pa.paged_attention_workspace_bytes(8, 32, 128, 512, 512) == 0
-    rows = 8 * 32 * 64
+    ws = pa.paged_attention_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
-    assert pa.paged_attention_workspace_bytes(8, 32, 128, 32768, 512) == \
-        2 * up(rows * 4) + up(rows * 128 * 4)
-    assert lib.pa_paged_attention_workspace_bytes(-1, 32, 128, 10, 16) == 0
+    size = lambda rows, d: 2 * up(rows * 4) + up(rows * d * 4)   # fixed split: no segment words
+    assert ws(8, 32, 32, 128, 32768, 0, pa.PA_BF16) == 0          # no split
+    assert ws(8, 32, 32, 128, 512, 512, pa.PA_BF16) == 0          # one partition each
+    # MHA: one row per (sequence, query head, partition).
+    assert ws(8, 32, 32, 128, 32768, 512, pa.PA_BF16) == size(8 * 32 * 64, 128)
+    # GQA on the MFMA path: a unit is a KV head holding G = 4 query heads.
+    assert ws(8, 32, 8, 128, 32768, 512, pa.PA_BF16) == size(8 * 8 * 64 * 4, 128)
+    # G = 32 > 16: two 16-head tiles per KV head.
+    assert ws(2, 64, 2, 64, 1024, 256, pa.PA_BF16) == size(2 * 4 * 4 * 16, 64)
+    # fp32 GQA runs one query head per unit.
+    assert ws(2, 64, 2, 64, 1024, 256, pa.PA_FP32) == size(2 * 64 * 4, 64)
+    assert lib.pa_paged_attention_workspace_bytes(-1, 32, 8, 128, 10, 16, pa.PA_BF16) == 0
+    assert lib.pa_paged_attention_workspace_bytes(4, 30, 8, 128, 10, 16, pa.PA_BF16) == 0
+    assert lib.pa_paged_attention_workspace_bytes(4, 32, 8, 128, 10, 16, 9) == 0
 
 
 def test_cache_calls_reject_bad_arguments():
@@ -92,3 +102,15 @@ def test_cache_calls_reject_bad_arguments():
         pa.PA_ERR_INVALID_ARG
     assert lib.pa_copy_blocks(NULL, NULL, NULL, -1, 8, 128, 16, 10, pa.PA_BF16, NULL) == \
         pa.PA_ERR_INVALID_ARG
+
+
+def test_balance_weights_are_validated():
+    pa.set_balance_weights([1, 2, 3, 4, 5, 6, 7, 8])
+    pa.set_balance_weights(None)
+    with pytest.raises(pa.PagedAttnError):
+        pa.set_balance_weights([100] * 7)
+    with pytest.raises(pa.PagedAttnError):
+        pa.set_balance_weights([100, 0, 100, 100, 100, 100, 100, 100])
+    with pytest.raises(pa.PagedAttnError):
+        pa.set_balance_weights([100] * 7 + [1001])
+    pa.set_balance_weights(None)

@@ -15,8 +15,8 @@ from tests.gpu_helpers import TOL, gpu_decode, max_abs_err, oracle_decode, to_de
 pytestmark = pytest.mark.gpu
 
 
-def _check(pa, case, ps, out_dtype=None, idx=None):
-    out = gpu_decode(pa, case, partition_size=ps, out_dtype=out_dtype)
+def _check(pa, case, ps, out_dtype=None, idx=None, kv_reused=False):
+    out = gpu_decode(pa, case, partition_size=ps, out_dtype=out_dtype, kv_reused=kv_reused)
     ref = oracle_decode(case, idx=idx)
     got = out if idx is None else out[torch.as_tensor(idx, device="cuda")]
     assert torch.isfinite(out.float()).all()
@@ -50,12 +50,15 @@ SMALL = [
 ]
 
 
+BAL = -1   # balanced split
+
+
 @pytest.mark.parametrize("name,kw", SMALL)
-@pytest.mark.parametrize("ps", [0, "bs", 64, 512])
+@pytest.mark.parametrize("ps", [0, "bs", 64, 512, BAL])
 def test_small_cases_match_oracle(gpu, name, kw, ps):
     case = W.make_case(name, device="cuda", **kw)
     ps = case.block_size if ps == "bs" else ps
-    if ps and ps % case.block_size:
+    if ps > 0 and ps % case.block_size:
         pytest.skip("partition size must be a multiple of the block size")
     _check(gpu, case, ps)
 
@@ -67,12 +70,14 @@ def test_fp32_and_bf16_outputs(gpu, name, kw):
     case = W.make_case(name, device="cuda", **kw)
     for od in (torch.float32, torch.bfloat16):
         _check(gpu, case, 64, out_dtype=od)
+        _check(gpu, case, BAL, out_dtype=od)
 
 
 # Full-size workloads, launched as the benchmark launches them, checked on
 # sampled sequences the oracle computes one by one.
 FULL = [("7b", {}, 512), ("70b", {}, 512), ("long", {}, 512), ("long", dict(block_size=32), 512),
-        ("7b", {}, 0)]
+        ("7b", {}, 0), ("7b", {}, BAL), ("70b", {}, BAL), ("long", {}, BAL),
+        ("long", dict(block_size=32), BAL)]
 
 
 @pytest.mark.parametrize("name,kw,ps", FULL)
@@ -83,11 +88,35 @@ def test_full_size_workloads_on_sampled_sequences(gpu, name, kw, ps):
     _check(gpu, case, ps, idx=idx)
 
 
+@pytest.mark.parametrize("name,kw", [("7b", dict(batch=6, len_range=(1, 3000))),
+                                     ("70b", dict(batch=6, len_range=(1, 3000))),
+                                     ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=16,
+                                                 num_kv_heads=1)),
+                                     ("tiny", {})])
+def test_reused_kv_loads_match_oracle_and_streaming(gpu, name, kw):
+    """The reuse flag changes only how K/V are loaded and, for the balanced
+    split, how the work is divided: fixed splits must be bit-identical to
+    the streaming loads, balanced ones must agree with the oracle."""
+    case = W.make_case(name, device="cuda", **kw)
+    for ps in (0, 64, BAL):
+        out, _ = _check(gpu, case, ps, kv_reused=True)
+        if ps >= 0:
+            assert torch.equal(out, gpu_decode(gpu, case, partition_size=ps))
+
+
+@pytest.mark.parametrize("name", ["7b", "70b"])
+def test_full_size_reused_balanced_split_on_sampled_sequences(gpu, name):
+    """Full 7B/70B batches divide evenly over the XCDs: the per-XCD split runs."""
+    case = W.make_case(name, device="cuda")
+    idx = np.sort(np.random.default_rng(9).choice(case.batch, size=6, replace=False))
+    _check(gpu, case, BAL, idx=idx, kv_reused=True)
+
+
 def test_empty_sequences_give_zero_rows(gpu):
     case = W.make_case("70b", device="cuda", batch=4, len_range=(20, 90))
     lens = case.context_lens.copy()
     lens[[1, 3]] = 0
-    for ps in (0, 32):
+    for ps in (0, 32, BAL):
         out = gpu_decode(gpu, case, partition_size=ps, lens=lens)
         assert torch.all(out[[1, 3]] == 0)
         ref = oracle_decode(case, lens=lens)
@@ -99,13 +128,15 @@ def test_permuting_physical_blocks_is_bit_identical(gpu):
                      ("70b", dict(batch=4, len_range=(40, 400))),
                      ("tiny", {})):
         case = W.make_case(name, device="cuda", **kw)
-        base = gpu_decode(gpu, case, partition_size=64)
         pi = torch.from_numpy(np.random.default_rng(3).permutation(case.num_blocks)).cuda()
         kc = torch.empty_like(case.key_cache); kc[pi] = case.key_cache
         vc = torch.empty_like(case.value_cache); vc[pi] = case.value_cache
         tab = pi.cpu().numpy()[case.block_tables].astype(np.int32)
-        moved = gpu_decode(gpu, case, partition_size=64, tables=tab, key_cache=kc, value_cache=vc)
-        assert torch.equal(base, moved)
+        for ps in (64, BAL):
+            base = gpu_decode(gpu, case, partition_size=ps)
+            moved = gpu_decode(gpu, case, partition_size=ps, tables=tab, key_cache=kc,
+                               value_cache=vc)
+            assert torch.equal(base, moved)
 
 
 def test_shared_prefix_blocks_give_bit_identical_outputs(gpu):
@@ -166,7 +197,7 @@ def test_nan_poisoned_pool_and_bad_padding_entries_are_never_used(gpu):
         for i, L in enumerate(case.context_lens):
             tab[i, -(-int(L) // case.block_size):] = case.num_blocks + 1000 + i
         clean = gpu_decode(gpu, case, partition_size=32)
-        for ps in (0, 32):
+        for ps in (0, 32, BAL):
             out = gpu_decode(gpu, case, partition_size=ps, tables=tab, key_cache=kc,
                              value_cache=vc)
             assert torch.isfinite(out.float()).all()
@@ -181,6 +212,20 @@ def test_run_to_run_determinism(gpu):
     case = W.make_case("7b", device="cuda", batch=8, len_range=(100, 1200))
     outs = [gpu_decode(gpu, case, partition_size=0) for _ in range(3)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    for name in ("7b", "70b"):
+        case = W.make_case(name, device="cuda", batch=16, len_range=(1, 3000))
+        outs = [gpu_decode(gpu, case, partition_size=BAL) for _ in range(3)]
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_balanced_split_of_one_huge_and_many_empty_sequences(gpu):
+    """Most waves land inside one long sequence; empty rows must come out zero."""
+    case = W.make_case("long", device="cuda", batch=6, lens=(0, 20000, 0, 3, 0, 0))
+    out, _ = _check(gpu, case, BAL)
+    assert torch.all(out[[0, 2, 4, 5]] == 0)
+    case = W.make_case("70b", device="cuda", batch=3, lens=(0, 0, 0))
+    out = gpu_decode(gpu, case, partition_size=BAL, max_context_len=16)
+    assert torch.all(out == 0)
 
 
 def test_deep_validation_rejects_bad_tables_without_launching(gpu, monkeypatch):
@@ -234,3 +279,21 @@ def test_timing_hook_brackets_the_main_kernel(gpu):
     assert 0 < main <= whole
     ref = oracle_decode(case, idx=[0, 5])
     assert max_abs_err(step.out[[0, 5]], ref) <= TOL["bf16"]
+
+
+def test_balanced_results_do_not_depend_on_xcd_weights(gpu):
+    """Weights move range boundaries (and so the merge order) but every
+    setting must agree with the oracle, and each setting is deterministic."""
+    for name, kw in (("70b", dict(batch=12, len_range=(1, 2500))),
+                     ("7b", dict(batch=12, len_range=(1, 2500)))):
+        case = W.make_case(name, device="cuda", **kw)
+        ref = oracle_decode(case)
+        try:
+            for w in ([100] * 8, [1, 1000, 1, 1000, 1, 1000, 1, 1000], None):
+                gpu.set_balance_weights(w)
+                a = gpu_decode(gpu, case, partition_size=BAL)
+                b = gpu_decode(gpu, case, partition_size=BAL)
+                assert torch.equal(a, b)
+                assert max_abs_err(a, ref) <= TOL[case.dtype]
+        finally:
+            gpu.set_balance_weights(None)
