@@ -44,6 +44,9 @@ WORKLOADS = {
 }
 
 
+MODEL_LAYERS = {"7b": 32, "70b": 80}
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -66,22 +69,47 @@ def build_step(name, ps, device):
                                                           num_blocks=case.num_blocks)
 
 
+def unique_kv_tokens(step, lens):
+    """Cached token slots the attention must read at least once: a physical
+    block shared by several sequences counts once, with the most tokens any
+    of them uses."""
+    tabs = step.block_tables.cpu().numpy()
+    used = {}
+    bs = step.block_size
+    for i, L in enumerate(lens.tolist()):
+        nb = -(-int(L) // bs)
+        for j in range(nb):
+            b = int(tabs[i, j])
+            used[b] = max(used.get(b, 0), min(bs, int(L) - j * bs))
+    return sum(used.values())
+
+
 def algorithmic_bytes(step, lens):
-    """Bytes the attention op must move: each KV head's tokens once (K and V),
-    q in, out back, the used table entries and the lengths."""
+    """(logical KV bytes, bytes the attention launch must move).
+
+    Logical: every sequence's K and V for every KV head, as the op consumes
+    them.  Launch: each distinct cached token once (K and V), q in, out
+    back, the used table entries and the lengths."""
     B, hq, d = step.query.shape
     esz = step.query.element_size()
-    kv = int(lens.sum()) * step.num_kv_heads * d * 2 * esz
+    per_token = step.num_kv_heads * d * 2 * esz
+    kv = int(lens.sum()) * per_token
     qo = B * hq * d * (esz + step.out.element_size())
     tables = 4 * int(np.sum(-(-lens // step.block_size))) + 4 * B
-    return kv, kv + qo + tables
+    return kv, unique_kv_tokens(step, lens) * per_token + qo + tables
 
 
 def kernel_source_digest():
+    """Digest of the device sources with comments and blank space removed:
+    it changes when the kernels' code changes, not when their comments do."""
+    import re
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_cache.hip"):
-        with open(os.path.join(ROOT, "paged_kv_cache_305_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("pa_decode.hip", "pa_cache.hip", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_305_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -100,7 +128,9 @@ def counter_traffic(workload, ps):
 
 
 def cpu_baseline(step, lens, max_seconds):
-    """The oracle, as it stands, on this host's cores, over a bounded sample."""
+    """The oracle, as it stands, on this host's cores, over a bounded sample:
+    consecutive sequences of the step (wrapping around the batch), in chunks
+    that double while they fit, until about max_seconds of wall time."""
     import oracle
     import workloads as W
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -110,10 +140,9 @@ def cpu_baseline(step, lens, max_seconds):
     tab = step.block_tables.cpu().numpy()
     ln = step.context_lens.cpu().numpy()
     B = q.shape[0]
-    # Grow the sample (a prefix of the batch) until it costs ~max_seconds.
-    n, spent, done_bytes, done_seqs = 1, 0.0, 0, 0
-    start = 0
-    while start < B and spent < max_seconds:
+    per_seq_bytes = lens * step.num_kv_heads * step.head_dim * 2 * step.query.element_size()
+    n, spent, done_bytes, done_seqs, start = 1, 0.0, 0, 0, 0
+    while spent < max_seconds:
         n = min(n, B - start)
         t0 = time.perf_counter()
         oracle.paged_attention(q[start:start + n], kc, vc, tab[start:start + n],
@@ -121,17 +150,17 @@ def cpu_baseline(step, lens, max_seconds):
                                head_dim=step.head_dim, block_size=step.block_size,
                                scale=step.scale, num_blocks=step.num_blocks, threads=threads)
         spent += time.perf_counter() - t0
-        done_bytes += int(lens[start:start + n].sum()) * step.num_kv_heads * step.head_dim * 2 * \
-            step.query.element_size()
+        done_bytes += int(per_seq_bytes[start:start + n].sum())
         done_seqs += n
-        start += n
+        start = (start + n) % B
         per_seq = spent / done_seqs
-        n = max(1, min(2 * n, int((max_seconds - spent) / per_seq)))
+        n = max(1, min(2 * n, B, int((max_seconds - spent) / per_seq)))
     return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=threads,
                 kind="oracle", seconds=round(spent, 3),
                 tokens_per_s=round(done_seqs / spent, 3),
-                sample="first %d of %d sequences of the same step (fp64 gather + naive softmax "
-                       "attention, %d threads)" % (done_seqs, B, threads))
+                sample="%d sequence-attentions (%.2f passes over the step's %d sequences), fp64 "
+                       "gather + naive softmax attention, %d threads" % (
+                           done_seqs, done_seqs / B, B, threads))
 
 
 def copy_calibration(device, steps):
@@ -228,7 +257,8 @@ def main():
     roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=counter_traffic(args.workload, args.partition_size),
-                algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2))
+                algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
+                kernel_source_digest=kernel_source_digest())
     result = {
         "metric": "paged decode attention KV GB/s (fraction of HBM peak) and tokens/s",
         "value": round(gbs, 1),
@@ -249,6 +279,11 @@ def main():
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / t_step, 1),
         "kv_tokens_per_s": round(float(lens.sum()) / t_step, 1),
+        # This step (cache write + attention) repeated for every layer of a
+        # model of this shape (32 layers for the 7B shape, 80 for the 70B
+        # shape), nothing else of the model: B / (t_step * layers).
+        **({"attn_only_model_tokens_per_s": round(B / (t_step * MODEL_LAYERS[args.workload]), 1)}
+           if args.workload in MODEL_LAYERS else {}),
         "step_ms_median": round(float(np.median(step_ms)), 4),
         "step_ms_min": round(float(np.min(step_ms)), 4),
         "wall_s_timed_loop": round(wall, 4),

@@ -11,7 +11,7 @@
 // The work is cut into segments, one per (sequence, head unit), each a run
 // of 16-token tiles (a 32-token block is two tiles).  A wave64 processes a
 // piece -- a contiguous tile range of one segment -- keeping the running
-// max / sum / output in registers and PF tiles of K/V loads in flight.  A
+// max / sum / output in registers and the next tile's K/V loads in flight.  A
 // piece covering its whole segment writes the output row; any other piece
 // writes a partial (max, sum, unnormalised output) that decode_merge
 // combines exactly by log-sum-exp.
@@ -61,10 +61,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short mfma_i16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float mfma_f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef PA_PREFETCH
-#define PA_PREFETCH 2
-#endif
-constexpr int kPrefetch = PA_PREFETCH;   // tiles of K/V loads kept in flight per wave
 
 struct bf16_t {
   uint16_t bits;
@@ -276,12 +272,6 @@ struct LenWindow {
   }
 };
 
-#ifdef PA_WAVES_PER_EU
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
-#else
-#define PA_OCCUPANCY
-#endif
-
 // ---- the streaming driver ----------------------------------------------------
 //
 // A wave walks its pieces as one continuous stream of tiles, two tile
@@ -394,6 +384,10 @@ struct ValuBody {
   static constexpr int RPI = 64 / LPR;             // value rows per load
   static constexpr int VJ = D / RPI;               // value loads per lane per tile
   static constexpr int TPB = BS / 16;              // tiles per block
+  // A 16-token tile of a 32-token block reads half of each value row; the
+  // other half belongs to the next tile, so those lines are loaded normally
+  // to let the second read hit.
+  static constexpr bool NTV = NT && TPB == 1;
   static_assert(KJ >= 1 && VJ >= 1, "unsupported shape");
 
   struct Tile {
@@ -451,7 +445,7 @@ struct ValuBody {
     for (int j = 0; j < KJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + t) * X);
 #pragma unroll
     for (int j = 0; j < VJ; ++j)
-      tl.v[j] = load_kv<u32x4, NT>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X);
+      tl.v[j] = load_kv<u32x4, NTV>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X);
   }
 
   __device__ static void init(Acc &a) {
@@ -550,6 +544,8 @@ struct MfmaBody {
   static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   static constexpr int VT = D / 16;   // 16-feature output tiles
   static constexpr int TPB = BS / 16;
+  // Value rows of a 32-token block are shared by two tiles: see ValuBody.
+  static constexpr bool NTV = NT && TPB == 1;
 
   struct Tile {
     u32x4 k[QJ];
@@ -612,7 +608,7 @@ struct MfmaBody {
 #pragma unroll
     for (int j = 0; j < QJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + c) * 8);
 #pragma unroll
-    for (int i = 0; i < VT; ++i) tl.v[i] = load_kv<u32x2, NT>(vb + (16 * i + c) * BS + 4 * g);
+    for (int i = 0; i < VT; ++i) tl.v[i] = load_kv<u32x2, NTV>(vb + (16 * i + c) * BS + 4 * g);
   }
 
   __device__ static void init(Acc &a) {
@@ -712,7 +708,7 @@ struct OnePiece {
 };
 
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
+__global__ __launch_bounds__(64) void decode_fixed(Params p) {
   __shared__ float p_lds[2][16];
   int id = (int)blockIdx.x;
   const int unit = id % p.units;
@@ -769,11 +765,7 @@ __device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
 
 // Two waves per SIMD at least: a single resident wave cannot keep enough
 // bytes in flight.
-#ifdef PA_WAVES_PER_EU
-#define PA_BALANCED_OCCUPANCY PA_OCCUPANCY
-#else
 #define PA_BALANCED_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
-#endif
 
 // Balanced split.  Sub-problem x (of xsplit) holds the head units
 // u = x + xsplit*k, k < Ux = units / xsplit, of every sequence, and the waves
