@@ -4,9 +4,11 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
 the host block allocator reserves each sequence's slot (copy-on-write pairs
 where a shared block is written; done once, outside the timed region), then
-on the GPU copy_blocks on those pairs, reshape_and_cache of each sequence's
-new token, and paged_attention_decode over all cached tokens (main kernel,
-plus the log-sum-exp merge when a sequence spans several partitions).
+on the GPU copy_blocks on those pairs, and the attention over all cached
+tokens (main kernel, plus the log-sum-exp merge when a sequence spans
+several pieces).  Each sequence's new token is written into its slot either
+by that launch or by reshape_and_cache just before it (--cache-write; by
+default the launch writes when the batch has few (sequence, KV head) rows).
 
 Timing: W warm-up steps, then K timed steps.  Before each step a 1 GiB
 buffer is read to evict the L2s and the Infinity Cache (outside the
@@ -185,6 +187,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per split-K partition; 0 = none, -1 = balanced split")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--cache-write", choices=["auto", "fused", "separate"], default="auto",
+                    help="write the new tokens inside the attention launch (fused), with "
+                         "reshape_and_cache before it (separate), or by batch size (auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,8 +216,12 @@ def main():
 
     log("building workload %s" % args.workload)
     step, lens, info = build_step(args.workload, args.partition_size, device)
+    step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
+    if step.uses_fused_write:   # the launch also reads and stores each new token's K and V
+        attn_bytes += 2 * step.new_key.numel() * step.new_key.element_size() * 2 + \
+            step.slot_mapping.numel() * 8
     flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=device)
     K, W_ = args.steps, args.warmup
     def ev():
@@ -275,6 +284,8 @@ def main():
         "config": {"workload": WORKLOADS[args.workload], "partition_size": args.partition_size,
                    "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
                    "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
+                   "cache_write": "inside the attention launch" if step.uses_fused_write
+                                  else "reshape_and_cache before the attention",
                    "flush_between_steps": flush is not None, **info},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / t_step, 1),

@@ -125,8 +125,42 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                                     uint32_t flags, void *workspace, size_t workspace_bytes,
                                     void *stream);
 
-/* Tracing hook: while set, every pa_paged_attention_decode call records
- * hipEvent_t `before_main` just before its main attention kernel and
+/* ------------------------------------------------------------------------
+ * paged_attention_decode_append -- one decode step's cache write and
+ * attention in one launch: the same results as pa_reshape_and_cache(new_key,
+ * new_value, key_cache, value_cache, slot_mapping, num_seqs, ...) followed by
+ * pa_paged_attention_decode(...) on the same stream, pools and outputs
+ * alike.  The new token of a sequence is the last of its context (the
+ * caller has reserved it with pa_seq_append_slot, which allocates a block at
+ * a block boundary and copies a shared block first; note-023 "Method" and
+ * "Concepts").  The wave that loads the 16-token tile holding that position
+ * puts the new token into the loaded registers and writes the tile back,
+ * so the write costs whole-burst stores instead of a separate pass of
+ * scattered ones, and the arithmetic is exactly the unfused pair's.
+ *
+ *  new_key, new_value  [num_seqs][num_kv_heads][head_dim] in kv_dtype (device)
+ *  slot_mapping   int64 [num_seqs] (device).  For each i, either negative
+ *                 (no new token: sequence i is attended as is) or the slot
+ *                 of position context_lens[i] - 1 in block_tables row i,
+ *                 in a block that no other sequence of the call reads or
+ *                 writes (true of blocks from pa_seq_append_slot, which
+ *                 copies a shared block first).  The other tokens of that
+ *                 tile are rewritten with the bytes just read from them.
+ *                 PA_VALIDATE=1 checks the position; a slot outside the pool
+ *                 is skipped like a negative one.
+ *  Every other argument as in pa_paged_attention_decode (key_cache and
+ *  value_cache are written here).
+ * ---------------------------------------------------------------------- */
+pa_status pa_paged_attention_decode_append(
+    void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
+    const void *new_value, const int64_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
+    pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Tracing hook: while set, every pa_paged_attention_decode(_append) call
+ * records hipEvent_t `before_main` just before its main attention kernel and
  * `after_main` just after it, on the call's stream (the log-sum-exp merge
  * kernel, when launched, comes after `after_main`).  Pass NULL, NULL to
  * stop.  The events are caller-owned; the setting is process-wide and not
@@ -142,7 +176,7 @@ pa_status pa_set_timing_events(void *before_main, void *after_main);
  * Process-wide; affects performance only, never results. */
 pa_status pa_set_balance_weights(const int32_t *weights, int32_t n);
 
-/* Bytes of workspace pa_paged_attention_decode needs for these sizes on the
+/* Bytes of workspace pa_paged_attention_decode (and _append) needs for these sizes on the
  * current device; 0 when every output row is written directly (no split).
  * Returns 0 for invalid arguments too (the decode call then reports them),
  * and for a balanced split when no device can be queried. */

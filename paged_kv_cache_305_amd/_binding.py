@@ -32,7 +32,8 @@ PA_DECODE_KV_REUSED = 1
 # Every symbol include/pagedattn.h declares.
 EXPORTS = (
     "pa_last_error", "pa_version",
-    "pa_paged_attention_decode", "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
+    "pa_paged_attention_decode", "pa_paged_attention_decode_append",
+    "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
     "pa_set_balance_weights",
     "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free",
@@ -61,6 +62,9 @@ def _declare(lib):
         "pa_paged_attention_decode": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             i64, i32, f32, i32, i32, i32, ctypes.c_uint32, vp, sz,
                                             vp]),
+        "pa_paged_attention_decode_append": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                   i32, i32, i32, i32, i64, i32, f32, i32, i32,
+                                                   i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_set_timing_events": (i32, [vp, vp]),
         "pa_set_balance_weights": (i32, [vp, i32]),
@@ -217,13 +221,18 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                            num_kv_heads: int, block_size: int, max_context_len: int,
                            scale: float, partition_size: int = 0, workspace=None,
                            num_blocks: Optional[int] = None, kv_reused: bool = False,
-                           stream=None):
+                           new_key=None, new_value=None, slot_mapping=None, stream=None):
     """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables.
 
     kv_reused: some physical blocks are read by several sequences (shared
-    prefixes): keep K/V in the caches instead of streaming them."""
+    prefixes): keep K/V in the caches instead of streaming them.
+
+    new_key, new_value ([B, Hkv, d]) and slot_mapping (int64 [B]), given
+    together: each sequence's last position is this new token, written into
+    its slot by the same launch (pa_paged_attention_decode_append)."""
     lib = load()
     dev = query.device
+    appending = new_key is not None or new_value is not None or slot_mapping is not None
     for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
                  (value_cache, "value_cache"), (block_tables, "block_tables"),
                  (context_lens, "context_lens")):
@@ -244,18 +253,36 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     chunk = num_kv_heads * d * block_size
     if key_cache.numel() < nb * chunk or value_cache.numel() < nb * chunk:
         raise ValueError("pools hold fewer than num_blocks blocks")
+    if appending:
+        if new_key is None or new_value is None or slot_mapping is None:
+            raise ValueError("new_key, new_value and slot_mapping go together")
+        for t, n in ((new_key, "new_key"), (new_value, "new_value"),
+                     (slot_mapping, "slot_mapping")):
+            _dev(t, n, dev)
+        if tuple(new_key.shape) != (B, num_kv_heads, d) or new_value.shape != new_key.shape:
+            raise ValueError("new_key and new_value must be [num_seqs, num_kv_heads, head_dim]")
+        if new_key.dtype != query.dtype or new_value.dtype != query.dtype:
+            raise TypeError("new_key and new_value must have the pools' dtype")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
+            raise ValueError("slot_mapping must be int64 [num_seqs]")
     need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
                                            partition_size, query.dtype)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (
         _dev(workspace, "workspace", dev).data_ptr(), workspace.numel() * workspace.element_size())
-    _check(lib.pa_paged_attention_decode(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
-        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(partition_size),
-        _dtype_code(query), _dtype_code(out), PA_DECODE_KV_REUSED if kv_reused else 0, ws_ptr,
-        ws_bytes, _stream(dev, stream)))
+    tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
+            int(block_tables.shape[1]), nb, int(max_context_len), float(scale),
+            int(partition_size), _dtype_code(query), _dtype_code(out),
+            PA_DECODE_KV_REUSED if kv_reused else 0, ws_ptr, ws_bytes, _stream(dev, stream))
+    if appending:
+        _check(lib.pa_paged_attention_decode_append(
+            out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(), *tail))
+    else:
+        _check(lib.pa_paged_attention_decode(
+            out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            *tail))
     return out
 
 

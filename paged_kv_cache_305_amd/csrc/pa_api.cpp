@@ -143,17 +143,21 @@ size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
       .total;
 }
 
-pa_status pa_paged_attention_decode(void *out, const void *query, const void *key_cache,
-                                    const void *value_cache, const int32_t *block_tables,
-                                    const int32_t *context_lens, int32_t num_seqs,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t block_size, int32_t max_blocks_per_seq,
-                                    int64_t num_blocks, int32_t max_context_len, float scale,
-                                    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
-                                    uint32_t flags, void *workspace, size_t workspace_bytes,
-                                    void *stream) {
-  pa_clear_error();
-  const char *fn = "pa_paged_attention_decode";
+}  // extern "C"
+
+namespace {
+
+// Shared by pa_paged_attention_decode (new_key == nullptr) and
+// pa_paged_attention_decode_append.
+pa_status decode_call(const char *fn, void *out, const void *query, const void *key_cache,
+                      const void *value_cache, const void *new_key, const void *new_value,
+                      const int64_t *slot_mapping, const int32_t *block_tables,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                      float scale, int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
+                      uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+  const bool appending = new_key != nullptr || new_value != nullptr || slot_mapping != nullptr;
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return pa_fail(PA_ERR_INVALID_ARG,
@@ -183,6 +187,13 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
     return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
     return pa_fail(PA_ERR_INVALID_ARG, "%s: out, query and pools must be 16-byte aligned", fn);
+  if (appending) {
+    if (!new_key || !new_value || !slot_mapping)
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: new_key, new_value and slot_mapping are all "
+                     "needed", fn);
+    if (!aligned16(new_key) || !aligned16(new_value))
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: new_key and new_value must be 16-byte aligned", fn);
+  }
 
   const int32_t parts = partitions_for(max_context_len, partition_size);
   const pa::HeadUnits hu = pa::head_units(num_q_heads, num_kv_heads, kv_dtype);
@@ -218,6 +229,24 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                          fn, i, j, b, (long long)num_blocks);
       }
     }
+    if (appending) {
+      // Each new token must sit at its sequence's last position.
+      std::vector<int64_t> slots;
+      s = to_host(slots, slot_mapping, (size_t)num_seqs, stream);
+      if (s != PA_OK) return s;
+      for (int32_t i = 0; i < num_seqs; ++i) {
+        if (slots[i] < 0) continue;
+        const int32_t pos = lens[i] - 1;
+        const int64_t want =
+            pos < 0 ? -1
+                    : (int64_t)tabs[(size_t)i * max_blocks_per_seq + pos / block_size] *
+                              block_size + pos % block_size;
+        if (slots[i] != want)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: slot_mapping[%d] = %lld is not the slot of "
+                         "position context_lens - 1 (%lld)", fn, i, (long long)slots[i],
+                         (long long)want);
+      }
+    }
   }
 
   pa::DecodeArgs a;
@@ -227,6 +256,9 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
   a.value_cache = value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.slots = slot_mapping;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -252,6 +284,42 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
   a.ev_after_main = g_ev_after_main;
   const int e = pa::launch_decode(a, stream);
   return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attention_decode(void *out, const void *query, const void *key_cache,
+                                    const void *value_cache, const int32_t *block_tables,
+                                    const int32_t *context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t max_blocks_per_seq,
+                                    int64_t num_blocks, int32_t max_context_len, float scale,
+                                    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
+                                    uint32_t flags, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  pa_clear_error();
+  return decode_call("pa_paged_attention_decode", out, query, key_cache, value_cache, nullptr,
+                     nullptr, nullptr, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, kv_dtype, out_dtype, flags,
+                     workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_append(
+    void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
+    const void *new_value, const int64_t *slot_mapping, const int32_t *block_tables,
+    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
+    pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+  pa_clear_error();
+  return decode_call("pa_paged_attention_decode_append", out, query, key_cache, value_cache,
+                     new_key, new_value, slot_mapping, block_tables, context_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, partition_size, kv_dtype, out_dtype,
+                     flags, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,

@@ -82,6 +82,28 @@ __device__ __forceinline__ float elem<bf16_t>(const u32x4 &c, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// Element e of a 16-byte chunk replaced by v (bit copy).  Written as
+// selects over constant indices: a runtime index into a vector register
+// would move the vector to scratch memory.
+template <typename KV>
+__device__ __forceinline__ u32x4 set_elem(u32x4 c, int e, KV v);
+template <>
+__device__ __forceinline__ u32x4 set_elem<float>(u32x4 c, int e, float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = k == e ? __float_as_uint(v) : c[k];
+  return c;
+}
+template <>
+__device__ __forceinline__ u32x4 set_elem<bf16_t>(u32x4 c, int e, bf16_t v) {
+  const unsigned lo = v.bits, hi = (unsigned)v.bits << 16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    c[k] = 2 * k == e ? ((c[k] & 0xffff0000u) | lo) : c[k];
+    c[k] = 2 * k + 1 == e ? ((c[k] & 0x0000ffffu) | hi) : c[k];
+  }
+  return c;
+}
+
 template <typename KV>
 __device__ __forceinline__ u32x4 zero_elem(u32x4 c, int e);
 template <>
@@ -182,10 +204,16 @@ __device__ __forceinline__ V load_kv(const void *ptr) {
 struct Params {
   void *out;
   const void *query;
-  const char *key_cache;
-  const char *value_cache;
+  char *key_cache;          // written only by the appending variant
+  char *value_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
+  // Appending variant (all null otherwise): the token at position L - 1 of
+  // sequence i is new_key/new_value[i], stored into slot slots[i] (< 0: no
+  // new token, position L - 1 is read from the cache like the others).
+  const void *new_key;
+  const void *new_value;
+  const int64_t *slots;
   float *ws_max, *ws_sum, *ws_acc;   // partial rows: [piece * gu + head in unit]
   int32_t *seg_units;                // balanced: per segment, first and last owning wave
   int64_t num_blocks;
@@ -215,8 +243,26 @@ struct Piece {
   int seq, unit;
   int t0, t1;       // tokens [t0, t1), t0 a multiple of 16
   bool whole;       // covers the whole segment: write the output row
+  bool last;        // ends where the segment ends (t1 = L)
   int64_t id;       // partial rows id * gu + h when !whole
+  // Set by the driver: the new token's slot when this piece ends with an
+  // appended token at t1 - 1, else -1.
+  int64_t slot;
 };
+
+// Slot of the token appended at the end of piece pc, or -1.  Out-of-range
+// slots count as none, so they are neither written nor substituted.
+template <int BS>
+__device__ __forceinline__ int64_t append_slot(const Params &p, const Piece &pc) {
+  if (p.slots == nullptr || !pc.last) return -1;
+  const int64_t s = p.slots[pc.seq];
+  return (s >= 0 && s < p.num_blocks * BS) ? s : -1;
+}
+
+// True when tile kt of piece pc holds the piece's appended token.
+__device__ __forceinline__ bool appends_in(const Piece &pc, int kt) {
+  return pc.slot >= 0 && kt == (pc.t1 - 1) >> 4;
+}
 
 // Block-table reader over blocks [first, first + count) of one table row:
 // 64 entries per VGPR chunk, read back with readlane.  Blocks are read in
@@ -298,6 +344,7 @@ __device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (
 
   Piece cp;                       // piece being computed
   if (!gen.next(cp)) return;
+  cp.slot = append_slot<BS>(p, cp);
   Piece lp = cp;                  // piece being loaded
   Piece pk;                       // peeked piece after lp (valid if has_pk)
   bool has_pk = gen.next(pk);
@@ -321,6 +368,7 @@ __device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (
       // Step into the peeked piece (its first table chunk is already
       // requested) and request its query.
       lp = pk;
+      lp.slot = append_slot<BS>(p, lp);
       tab = tab_pk;
       head_off = Body::head_offset(p, lp.unit);
       lk = lp.t0 >> 4;
@@ -455,8 +503,9 @@ struct ValuBody {
     for (int j = 0; j < VJ; ++j) a.o[j] = 0.f;
   }
 
-  __device__ static void compute(const Params &, const Piece &pc, const QReady &q, Acc &a,
+  __device__ static void compute(const Params &p, const Piece &pc, const QReady &q, Acc &a,
                                  Tile &tl, int kt, float (&p_lds)[2][16]) {
+    if (appends_in(pc, kt)) patch_tile(p, pc, tl, kt);
     const int lane = (int)threadIdx.x;
     const int t = lane & 15, vpiece = lane % LPR;
     float dot = 0.f;
@@ -493,6 +542,52 @@ struct ValuBody {
     for (int j = 0; j < VJ; ++j)
 #pragma unroll
       for (int e = 0; e < X; ++e) a.o[j] = fmaf(pv[e], elem<KV>(tl.v[j], e), a.o[j]);
+  }
+
+  // Put the appended token (position t1 - 1, lane row r0 of tile kt) into
+  // the loaded tile, as if it had been read from its slot, and -- from one
+  // query head of its group -- store the tile back: the value rows whole
+  // and the keys as the 64-byte runs of four tokens around r0, so every
+  // write covers whole 64-byte memory bursts.
+  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int kt) {
+    const int lane = (int)threadIdx.x;
+    const int t = lane & 15, g = lane >> 4, vpiece = lane % LPR;
+    const int r0 = (pc.t1 - 1) & 15;
+    const int kvh = pc.unit / p.group;
+    const int64_t src = ((int64_t)pc.seq * p.num_kv_heads + kvh) * D;
+    const KV *nk = static_cast<const KV *>(p.new_key) + src;
+    const KV *nv = static_cast<const KV *>(p.new_value) + src;
+    // Every lane loads and selects (no divergent branches): the compiler
+    // then waits once for these loads, and the stores below go out back to
+    // back with their data already in registers.
+    u32x4 kn[KJ];
+    KV vn[VJ];
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) kn[j] = *reinterpret_cast<const u32x4 *>(nk + (4 * j + g) * X);
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) vn[j] = nv[j * RPI + lane / LPR];
+    const bool krow = t == r0, vrow = r0 / X == vpiece;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) tl.k[j] = krow ? kn[j] : tl.k[j];
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) {
+      const u32x4 w = set_elem<KV>(tl.v[j], r0 % X, vn[j]);
+      tl.v[j] = vrow ? w : tl.v[j];
+    }
+    if (pc.unit % p.group != 0) return;
+    const int64_t blk = pc.slot / BS;
+    const int sub = (kt * 16) % BS / 16;
+    const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
+    KV *kb = reinterpret_cast<KV *>(p.key_cache) + base + sub * 16 * X;
+    KV *vb = reinterpret_cast<KV *>(p.value_cache) + base + sub * 16;
+    if ((t >> 2) == (r0 >> 2)) {
+#pragma unroll
+      for (int j = 0; j < KJ; ++j)
+        *reinterpret_cast<u32x4 *>(kb + ((4 * j + g) * BS + t) * X) = tl.k[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VJ; ++j)
+      *reinterpret_cast<u32x4 *>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X) = tl.v[j];
   }
 
   // Combine the sum over the 16 token lanes and each row over its LPR lanes,
@@ -620,6 +715,7 @@ struct MfmaBody {
 
   __device__ static void compute(const Params &p, const Piece &pc, const QReady &q, Acc &a,
                                  Tile &tl, int kt, float (&)[2][16]) {
+    if (appends_in(pc, kt)) patch_tile(p, pc, tl, kt);
     const int g = (int)threadIdx.x >> 4;
     mfma_f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -662,6 +758,51 @@ struct MfmaBody {
                                                          pb, a.o[i], 0, 0, 0);
   }
 
+  // Put the appended token (position t1 - 1, row r0 of tile kt) into the
+  // loaded tile, as if it had been read from its slot, and -- from the
+  // first head tile of its KV head -- store the tile back: the value rows
+  // whole and the keys as the 64-byte runs of four tokens around r0, so
+  // every write covers whole 64-byte memory bursts.
+  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int kt) {
+    const int lane = (int)threadIdx.x;
+    const int c = lane & 15, g = lane >> 4;
+    const int r0 = (pc.t1 - 1) & 15;
+    const int kvh = pc.unit / p.head_tiles;
+    const int64_t src = ((int64_t)pc.seq * p.num_kv_heads + kvh) * D;
+    const bf16_t *nk = static_cast<const bf16_t *>(p.new_key) + src;
+    const bf16_t *nv = static_cast<const bf16_t *>(p.new_value) + src;
+    // Every lane loads and selects (no divergent branches): see ValuBody.
+    u32x4 kn[QJ];
+    bf16_t vn[VT];
+#pragma unroll
+    for (int j = 0; j < QJ; ++j) kn[j] = *reinterpret_cast<const u32x4 *>(nk + (4 * j + g) * 8);
+#pragma unroll
+    for (int i = 0; i < VT; ++i) vn[i] = nv[16 * i + c];
+    const bool krow = c == r0, vrow = g == (r0 >> 2);
+    const int e = r0 & 3;
+#pragma unroll
+    for (int j = 0; j < QJ; ++j) tl.k[j] = krow ? kn[j] : tl.k[j];
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const u32x4 w = set_elem<bf16_t>(u32x4{tl.v[i][0], tl.v[i][1], 0u, 0u}, e, vn[i]);
+      tl.v[i] = vrow ? u32x2{w[0], w[1]} : tl.v[i];
+    }
+    if (pc.unit % p.head_tiles != 0) return;
+    const int64_t blk = pc.slot / BS;
+    const int sub = (kt * 16) % BS / 16;
+    const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
+    bf16_t *kb = reinterpret_cast<bf16_t *>(p.key_cache) + base + sub * 16 * 8;
+    bf16_t *vb = reinterpret_cast<bf16_t *>(p.value_cache) + base + sub * 16;
+    if ((c >> 2) == (r0 >> 2)) {
+#pragma unroll
+      for (int j = 0; j < QJ; ++j)
+        *reinterpret_cast<u32x4 *>(kb + ((4 * j + g) * BS + c) * 8) = tl.k[j];
+    }
+#pragma unroll
+    for (int i = 0; i < VT; ++i)
+      *reinterpret_cast<u32x2 *>(vb + (16 * i + c) * BS + 4 * g) = tl.v[i];
+  }
+
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
     const int g = (int)threadIdx.x >> 4, hh = (int)threadIdx.x & 15;
     float ltot = a.lsum + xor16(a.lsum);
@@ -692,6 +833,10 @@ struct MfmaBody {
 
 // ---- grid strategies ---------------------------------------------------------
 
+// Two waves per SIMD at least: a single resident wave cannot keep enough
+// bytes in flight.
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
+
 // Fixed partitions: workgroup id -> (unit, sequence, partition), the unit
 // varying fastest.  Consecutive workgroups go round-robin to the 8 XCDs, so
 // when the unit count is a multiple of 8 every workgroup of one head unit
@@ -708,7 +853,7 @@ struct OnePiece {
 };
 
 template <class Body>
-__global__ __launch_bounds__(64) void decode_fixed(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
   __shared__ float p_lds[2][16];
   int id = (int)blockIdx.x;
   const int unit = id % p.units;
@@ -731,8 +876,8 @@ __global__ __launch_bounds__(64) void decode_fixed(Params p) {
     return;
   }
   if (part >= nparts) return;
-  OnePiece gen{Piece{seq, unit, t0, t1, nparts == 1,
-                     ((int64_t)seq * p.units + unit) * p.num_partitions + part},
+  OnePiece gen{Piece{seq, unit, t0, t1, nparts == 1, part == nparts - 1,
+                     ((int64_t)seq * p.units + unit) * p.num_partitions + part, -1},
                false};
   stream_pieces<Body>(p, gen, p_lds);
 }
@@ -763,9 +908,6 @@ __device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
   return tot;
 }
 
-// Two waves per SIMD at least: a single resident wave cannot keep enough
-// bytes in flight.
-#define PA_BALANCED_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
 
 // Balanced split.  Sub-problem x (of xsplit) holds the head units
 // u = x + xsplit*k, k < Ux = units / xsplit, of every sequence, and the waves
@@ -821,8 +963,8 @@ struct RangePieces {
       if (a == 0) p->seg_units[2 * g] = (int32_t)unit;
       if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
     }
-    out = Piece{seq, u, a * 16, min(b * 16, L), a == 0 && b == n_seq,
-                id_base + (int64_t)seq * ux + k + unit};
+    out = Piece{seq, u, a * 16, min(b * 16, L), a == 0 && b == n_seq, b == n_seq,
+                id_base + (int64_t)seq * ux + k + unit, -1};
     t += len;
     a = 0;
     if (t < te && ++k == ux) {
@@ -841,7 +983,7 @@ struct RangePieces {
 };
 
 template <class Body>
-__global__ __launch_bounds__(64) PA_BALANCED_OCCUPANCY void decode_balanced(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   __shared__ float p_lds[2][16];
   const int lane = (int)threadIdx.x;
   RangePieces gen;
@@ -1061,10 +1203,14 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   Params p;
   p.out = a.out;
   p.query = a.query;
-  p.key_cache = static_cast<const char *>(a.key_cache);
-  p.value_cache = static_cast<const char *>(a.value_cache);
+  // The pools are written only when new tokens are given.
+  p.key_cache = static_cast<char *>(const_cast<void *>(a.key_cache));
+  p.value_cache = static_cast<char *>(const_cast<void *>(a.value_cache));
   p.block_tables = a.block_tables;
   p.context_lens = a.context_lens;
+  p.new_key = a.new_key;
+  p.new_value = a.new_value;
+  p.slots = a.slots;
   p.ws_max = a.ws_max;
   p.ws_sum = a.ws_sum;
   p.ws_acc = a.ws_acc;

@@ -17,6 +17,9 @@ struct DecodeArgs {
   void *out;
   const void *query, *key_cache, *value_cache;
   const int32_t *block_tables, *context_lens;
+  // Appending variant: new token per sequence and its slot (null otherwise).
+  const void *new_key, *new_value;
+  const int64_t *slots;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int64_t num_blocks;
   int32_t max_context_len;

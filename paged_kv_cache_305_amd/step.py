@@ -3,12 +3,14 @@
 Host: the block allocator reserves each sequence's next slot, allocating a
 block at a block boundary and returning a (src, dst) copy pair when the
 last block is shared (copy-on-write).  Device, in stream order: copy_blocks
-on the pairs, reshape_and_cache of the new tokens into their slots, then
-paged_attention_decode over every sequence's cached tokens.
+on the pairs, then the attention over every sequence's cached tokens with
+the new tokens written into their slots by the same launch
+(paged_attention_decode_append) -- or, unfused, reshape_and_cache followed
+by paged_attention_decode.  Both give the same pools and outputs.
 
 The host part runs once when the step is built; ``run()`` only launches the
-three kernels, so it can be repeated (same pairs, same slots, same reads)
-for timing.
+kernels, so it can be repeated (same pairs, same slots, same reads) for
+timing.
 """
 from __future__ import annotations
 
@@ -41,6 +43,10 @@ class DecodeStep:
     scale: float
     partition_size: int
     kv_reused: bool = False
+    # Write the new tokens from inside the attention launch (True), with
+    # reshape_and_cache first (False), or choose by the number of
+    # (sequence, KV head) rows written (None).
+    fused: Optional[bool] = None
 
     @property
     def num_pairs(self) -> int:
@@ -57,19 +63,40 @@ class DecodeStep:
                             self.slot_mapping, block_size=self.block_size,
                             num_blocks=self.num_blocks, stream=stream)
 
-    def attend(self, stream=None):
+    def attend(self, stream=None, append=False):
+        extra = dict(new_key=self.new_key, new_value=self.new_value,
+                     slot_mapping=self.slot_mapping) if append else {}
         B.paged_attention_decode(self.out, self.query, self.key_cache, self.value_cache,
                                  self.block_tables, self.context_lens,
                                  num_kv_heads=self.num_kv_heads, block_size=self.block_size,
                                  max_context_len=self.max_context_len, scale=self.scale,
                                  partition_size=self.partition_size, workspace=self.workspace,
                                  num_blocks=self.num_blocks, kv_reused=self.kv_reused,
-                                 stream=stream)
+                                 stream=stream, **extra)
+
+    # The in-launch write stores each new (token, KV head) as whole 64-byte
+    # bursts of the 16-token tile around it (about 5 KiB); on MI355X, with
+    # ~2000 such rows per step (the 7B and 70B-shaped batches) those writes
+    # slow the streaming reads by more than a separate reshape_and_cache
+    # costs, while with a few hundred rows (long contexts, shared prefixes)
+    # the saved launch wins.
+    FUSED_MAX_ROWS = 1024
+
+    @property
+    def uses_fused_write(self) -> bool:
+        if self.fused is not None:
+            return self.fused
+        return int(self.query.shape[0]) * self.num_kv_heads <= self.FUSED_MAX_ROWS
 
     def run(self, stream=None):
+        """copy_blocks, then either one launch that writes the new tokens and
+        attends (fused) or reshape_and_cache followed by attention."""
         self.copy(stream)
-        self.write(stream)
-        self.attend(stream)
+        if self.uses_fused_write:
+            self.attend(stream, append=True)
+        else:
+            self.write(stream)
+            self.attend(stream)
         return self.out
 
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(pa.load()._name)
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_version() == 100
+    assert lib.pa_version() == 101
 
 
 NULL = None
@@ -62,6 +62,23 @@ def test_decode_rejects_bad_arguments_before_launch(kw, status):
     lib = pa.load()
     assert _decode(lib, **kw) == status
     assert lib.pa_last_error()
+
+
+def test_append_needs_all_three_new_token_pointers():
+    lib = pa.load()
+    base = dict(out=16, query=32, key_cache=48, value_cache=64, new_key=NULL, new_value=NULL,
+                slot_mapping=NULL, block_tables=8, context_lens=8, num_seqs=1, num_q_heads=8,
+                num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4,
+                num_blocks=16, max_context_len=64, scale=0.1, partition_size=0,
+                kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16, flags=0, workspace=NULL,
+                workspace_bytes=0, stream=NULL)
+    for kw in (dict(new_key=80), dict(new_key=80, new_value=96),
+               dict(new_key=80, new_value=104, slot_mapping=8)):   # misaligned new_value
+        a = dict(base, **kw)
+        assert lib.pa_paged_attention_decode_append(*a.values()) == pa.PA_ERR_INVALID_ARG
+        assert lib.pa_last_error()
+    a = dict(base, num_seqs=0)
+    assert lib.pa_paged_attention_decode_append(*a.values()) == pa.PA_OK
 
 
 def test_decode_with_no_sequences_is_a_no_op():
