@@ -86,6 +86,32 @@ def unique_kv_tokens(step, lens):
     return sum(used.values())
 
 
+def block_waste(step, lens):
+    """Internal fragmentation of the step's cache: slots allocated in the
+    distinct blocks the tables reference, and the share of them no token
+    fills (each sequence wastes at most block_size - 1 slots of its last
+    block)."""
+    used = unique_kv_tokens(step, lens)
+    tabs = step.block_tables.cpu().numpy()
+    blocks = set()
+    for i, L in enumerate(lens.tolist()):
+        blocks.update(int(b) for b in tabs[i, :-(-int(L) // step.block_size)])
+    allocated = len(blocks) * step.block_size
+    return dict(kv_slots_allocated=allocated, kv_slots_used=used,
+                kv_block_waste_frac=round(1.0 - used / allocated, 5) if allocated else 0.0)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def algorithmic_bytes(step, lens):
     """(logical KV bytes, bytes the attention launch must move).
 
@@ -158,7 +184,7 @@ def cpu_baseline(step, lens, max_seconds):
         per_seq = spent / done_seqs
         n = max(1, min(2 * n, B, int((max_seconds - spent) / per_seq)))
     return dict(value=round(done_bytes / spent / 1e9, 4), unit="GB/s", cores=threads,
-                kind="oracle", seconds=round(spent, 3),
+                kind="oracle", seconds=round(spent, 3), cpu_model=cpu_model(),
                 tokens_per_s=round(done_seqs / spent, 3),
                 sample="%d sequence-attentions (%.2f passes over the step's %d sequences), fp64 "
                        "gather + naive softmax attention, %d threads" % (
@@ -286,7 +312,8 @@ def main():
                    "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
                    "cache_write": "inside the attention launch" if step.uses_fused_write
                                   else "reshape_and_cache before the attention",
-                   "flush_between_steps": flush is not None, **info},
+                   "flush_between_steps": flush is not None, **info,
+                   **block_waste(step, lens)},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / t_step, 1),
         "kv_tokens_per_s": round(float(lens.sum()) / t_step, 1),

@@ -54,7 +54,7 @@ BAL = -1   # balanced split
 
 
 @pytest.mark.parametrize("name,kw", SMALL)
-@pytest.mark.parametrize("ps", [0, "bs", 64, 512, BAL])
+@pytest.mark.parametrize("ps", [0, "bs", 64, 512, 1024, BAL])
 def test_small_cases_match_oracle(gpu, name, kw, ps):
     case = W.make_case(name, device="cuda", **kw)
     ps = case.block_size if ps == "bs" else ps
