@@ -43,7 +43,10 @@ WORKLOADS = {
               "32/8 heads, d 128, bf16, Bs 16, CoW step",
     "long": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 16",
     "long32": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 32",
+    "swap": "preemption swap of the 7B-shaped step's blocks: GPU pool <-> pinned host pool "
+            "(swap_blocks), both directions",
 }
+HOST_LINK_PEAK_GBS = 64.0   # PCIe Gen5 x16, one direction
 
 
 MODEL_LAYERS = {"7b": 32, "70b": 80}
@@ -191,6 +194,61 @@ def cpu_baseline(step, lens, max_seconds):
                            done_seqs, done_seqs / B, B, threads))
 
 
+def swap_bench(args, device):
+    """Time swap_blocks of every block the 7B-shaped step uses, out to a
+    pinned host pool and back in, each direction on its own."""
+    import torch
+    import paged_kv_cache_305_amd as pa
+    import workloads as W
+    case = W.make_case("7b", device=device)
+    used = np.unique(np.concatenate([case.block_tables[i, :-(-int(L) // case.block_size)]
+                                     for i, L in enumerate(case.context_lens)]))
+    n = int(used.shape[0])
+    hk = torch.empty((n,) + tuple(case.key_cache.shape[1:]), dtype=case.key_cache.dtype,
+                     pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_map = torch.from_numpy(np.stack([used, np.arange(n)], 1).astype(np.int64)).to(device)
+    in_map = torch.from_numpy(np.stack([np.arange(n), used], 1).astype(np.int64)).to(device)
+    kw = dict(num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+              block_size=case.block_size)
+    nbytes = 2 * n * case.key_cache[0].numel() * case.key_cache.element_size()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+
+    t_out = timed(lambda: pa.swap_blocks(hk, hv, case.key_cache, case.value_cache, out_map,
+                                         **kw))
+    t_in = timed(lambda: pa.swap_blocks(case.key_cache, case.value_cache, hk, hv, in_map, **kw))
+    ok = W.host_array(hk[:4]).tobytes() == W.host_array(case.key_cache[used[:4]]).tobytes()
+    out_gbs, in_gbs = nbytes / t_out / 1e9, nbytes / t_in / 1e9
+    result = {
+        "metric": "preemption swap GB/s (GPU pool <-> pinned host pool)",
+        "value": round((out_gbs + in_gbs) / 2, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t_out + t_in) * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the 7B-shaped step's K/V pools)",
+        "config": {"workload": WORKLOADS["swap"], "blocks": n, "bytes_each_way": nbytes,
+                   "swap_out_GBs": round(out_gbs, 2), "swap_in_GBs": round(in_gbs, 2),
+                   "copy_checked": ok},
+        "roofline": dict(bound="host link", achieved=round((out_gbs + in_gbs) / 2, 2),
+                         peak=HOST_LINK_PEAK_GBS, unit="GB/s",
+                         frac=round((out_gbs + in_gbs) / 2 / HOST_LINK_PEAK_GBS, 4),
+                         traffic=None),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def copy_calibration(device, steps):
     """A plain 1 GiB device copy, for scaling the FETCH/WRITE counters."""
     import torch
@@ -238,6 +296,9 @@ def main():
     torch.cuda.set_device(device)
     if args.copy_calibration:
         copy_calibration(device, max(1, args.steps))
+        return
+    if args.workload == "swap":
+        swap_bench(args, device)
         return
 
     log("building workload %s" % args.workload)

@@ -219,6 +219,30 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int64_t *bloc
                          int32_t block_size, int64_t num_blocks, pa_dtype dtype, void *stream);
 
 /* ------------------------------------------------------------------------
+ * swap_blocks -- the copy half of swapping a preempted sequence's blocks to
+ * host memory and back (inferensys glossary "Paged Attention", third and
+ * fifth paragraphs; crackai.dev "How It Works", preemption and swapping).
+ * Copies whole blocks, K and V, from one pool to another; either pool may
+ * be device memory or pinned host memory the device can address (from
+ * hipHostMalloc, e.g. a torch tensor with pin_memory=True), both in the
+ * pool layout above with the same head count, head size and block size.
+ * One launch for all pairs.
+ *
+ *  block_mapping  int64 [num_pairs][2], device-addressable: (block in src
+ *                 pools, block in dst pools), as pa_seqs_swap_out/_in
+ *                 return them.  dst blocks must be distinct.  Pairs with a
+ *                 block outside [0, src_num_blocks) or [0, dst_num_blocks)
+ *                 are skipped (PA_VALIDATE=1 rejects them).
+ *  Every pointer is checked with hipPointerGetAttributes before the launch:
+ *  pageable host memory gives PA_ERR_INVALID_ARG instead of a device fault.
+ * ---------------------------------------------------------------------- */
+pa_status pa_swap_blocks(void *dst_key_cache, void *dst_value_cache, const void *src_key_cache,
+                         const void *src_value_cache, const int64_t *block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t src_num_blocks, int64_t dst_num_blocks,
+                         pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
  * Block allocator (host).  Free list, reference counts and copy-on-write
  * over a pool of num_blocks physical blocks (note-023 "Method" and
  * "Concepts"; inferensys glossary, first and second paragraphs; crackai.dev
@@ -270,8 +294,9 @@ pa_status pa_seq_append_slot(pa_allocator *a, int64_t seq_id, int64_t *slot, int
  * reaching zero return to the free list (last logical block first). */
 pa_status pa_seq_free(pa_allocator *a, int64_t seq_id);
 
-/* Copy the sequence's physical blocks into out[0..capacity); *n_out gets the
- * count.  PA_ERR_INVALID_ARG if capacity is too small (nothing written). */
+/* Copy the sequence's physical blocks (swap-space blocks while it is
+ * swapped out) into out[0..capacity); *n_out gets the count.
+ * PA_ERR_INVALID_ARG if capacity is too small (nothing written). */
 pa_status pa_seq_block_table(const pa_allocator *a, int64_t seq_id, int32_t *out,
                              int32_t capacity, int32_t *n_out);
 
@@ -280,6 +305,38 @@ int64_t pa_seq_len(const pa_allocator *a, int64_t seq_id);
 
 /* References to a physical block (0 = free), or -1 if out of range. */
 int32_t pa_block_refcount(const pa_allocator *a, int32_t block);
+
+/* Swap space: num_host_blocks blocks in host memory with their own LIFO free
+ * list (first hand-outs 0, 1, 2, ...), replacing any previous swap space.
+ * PA_ERR_INVALID_ARG while a sequence is swapped out. */
+pa_status pa_allocator_set_swap_space(pa_allocator *a, int64_t num_host_blocks);
+int64_t pa_allocator_num_free_host(const pa_allocator *a);
+/* References to a swap-space block (0 = free), or -1 if out of range. */
+int32_t pa_host_block_refcount(const pa_allocator *a, int32_t block);
+/* 1 if the sequence is swapped out, 0 if resident, -1 if unknown. */
+int32_t pa_seq_is_swapped(const pa_allocator *a, int64_t seq_id);
+
+/* Preempt a group of resident sequences to the swap space (inferensys
+ * glossary, third and fifth paragraphs).  The group's distinct device
+ * blocks, in order of first appearance (sequences in the given order, each
+ * table in logical order), each get one swap block; pairs[2k], pairs[2k+1]
+ * = (device block, swap block) for pa_swap_blocks (host int64 array of
+ * capacity pairs), *num_pairs their count.  Each device block loses the
+ * group's references and returns to the free list at zero (in reverse order
+ * of first appearance), so the caller must run the copy before reusing the
+ * pool.  Blocks shared inside the group stay shared in the swap space.
+ * While swapped, a sequence cannot be forked, appended to or put in a
+ * table; pa_seq_free releases its swap blocks.  All-or-nothing:
+ * PA_ERR_OUT_OF_BLOCKS if the swap space is too small, PA_ERR_INVALID_ARG
+ * for a repeated, already swapped sequence or a small capacity. */
+pa_status pa_seqs_swap_out(pa_allocator *a, const int64_t *seq_ids, int32_t n, int64_t *pairs,
+                           int32_t capacity, int32_t *num_pairs);
+
+/* Bring a group of swapped-out sequences back: the mirror of
+ * pa_seqs_swap_out, pairs = (swap block, device block).  Generation resumes
+ * from the same tokens, in new device blocks. */
+pa_status pa_seqs_swap_in(pa_allocator *a, const int64_t *seq_ids, int32_t n, int64_t *pairs,
+                          int32_t capacity, int32_t *num_pairs);
 
 /* Pack the tables and lengths of n sequences for upload: out_tables is a
  * host int32 [n][max_blocks] filled with each table, padded with pad;

@@ -7,8 +7,9 @@ imports the product.
 
 Contents:
   * ``oracle.c`` -- plain C, fp64: gather-then-naive-softmax attention,
-    the reshape_and_cache scatter and the copy_blocks copy (see its header
-    for the passages each follows and the pool layout it addresses).
+    the reshape_and_cache scatter, the copy_blocks copy and the swap_blocks
+    copy between pools (see its header for the passages each follows and
+    the pool layout it addresses).
   * ``alloc_model`` -- a plain Python model of the block allocator.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against
@@ -52,8 +53,9 @@ def _load():
                                                i32, i64, ctypes.c_double, i32, i32]
         lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32]
         lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, i32]
+        lib.oracle_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32]
         for f in (lib.oracle_paged_attention, lib.oracle_reshape_and_cache,
-                  lib.oracle_copy_blocks):
+                  lib.oracle_copy_blocks, lib.oracle_swap_blocks):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -125,3 +127,20 @@ def copy_blocks(key_cache, value_cache, block_mapping, *, num_kv_heads: int, hea
         block_size, int(num_blocks), _dtype_code(key_cache))
     if rc != 0:
         raise ValueError("oracle_copy_blocks failed (%d)" % rc)
+
+
+def swap_blocks(dst_key, dst_value, src_key, src_value, block_mapping, *, num_kv_heads: int,
+                head_dim: int, block_size: int) -> None:
+    """Whole-block copies from the src pools into the (distinct) dst pools:
+    block t of dst becomes block s of src for each pair (s, t)."""
+    for a in (dst_key, dst_value):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("destination pools must be contiguous (written in place)")
+    m = _c(block_mapping, np.int64).reshape(-1, 2)
+    sk, sv = _c(src_key, src_key.dtype), _c(src_value, src_value.dtype)
+    rc = _load().oracle_swap_blocks(
+        _ptr(dst_key), _ptr(dst_value), _ptr(sk), _ptr(sv), _ptr(m), int(m.shape[0]),
+        num_kv_heads, head_dim, block_size, int(sk.shape[0]), int(dst_key.shape[0]),
+        _dtype_code(dst_key))
+    if rc != 0:
+        raise ValueError("oracle_swap_blocks failed (%d)" % rc)

@@ -23,6 +23,21 @@ Where the pages leave the policy open, this model takes these readings:
     append pops a fresh block instead;
   * every operation is all-or-nothing: on pool exhaustion or a bad id the
     state is unchanged.
+
+Swapping preempted sequences to host memory and back (inferensys glossary,
+third and fifth paragraphs; crackai.dev "How It Works", preemption and
+swapping), with these readings:
+  * the swap space is a second pool of block ids with its own LIFO free
+    list, first pops 0, 1, 2, ...;
+  * a group swap moves the distinct blocks of the given sequences, taken in
+    order of first appearance (sequences in the given order, each table in
+    logical order); each gets one block of the other pool, holding as many
+    references as the group makes to it;
+  * the old blocks lose those references, and the ones left unreferenced
+    are pushed back in reverse order of first appearance;
+  * a swapped sequence keeps its length (generation resumes where it
+    stopped) but cannot be forked, appended to or exported; freeing it
+    releases its swap blocks.
 """
 from __future__ import annotations
 
@@ -50,8 +65,11 @@ class BlockAllocatorModel:
         # Top of the stack is the end of the list: pops come out as order[0], order[1], ...
         self.free = list(reversed(order))
         self.refcount = [0] * num_blocks
-        self.tables = {}   # seq_id -> list of physical blocks
+        self.tables = {}   # seq_id -> list of physical blocks (swap blocks when swapped)
         self.lengths = {}  # seq_id -> tokens held
+        self.swapped = {}  # seq_id -> True while its blocks live in the swap space
+        self.host_free = []
+        self.host_refcount = []
 
     # --- queries -----------------------------------------------------------
     def num_free(self) -> int:
@@ -81,22 +99,28 @@ class BlockAllocatorModel:
             self.refcount[b] = 1
         self.tables[seq_id] = blocks
         self.lengths[seq_id] = num_tokens
+        self.swapped[seq_id] = False
 
     def fork(self, parent, child):
         if parent not in self.tables:
             raise AllocError(ERR_UNKNOWN_SEQ, "unknown parent %r" % (parent,))
         if child in self.tables:
             raise AllocError(ERR_INVALID_ARG, "child %r exists" % (child,))
+        if self.swapped[parent]:
+            raise AllocError(ERR_INVALID_ARG, "parent %r is swapped out" % (parent,))
         blocks = list(self.tables[parent])
         for b in blocks:
             self.refcount[b] += 1
         self.tables[child] = blocks
         self.lengths[child] = self.lengths[parent]
+        self.swapped[child] = False
 
     def append_slot(self, seq_id):
         """Reserve the next position; returns (slot, cow_src, cow_dst), -1 when no copy."""
         if seq_id not in self.tables:
             raise AllocError(ERR_UNKNOWN_SEQ, "unknown sequence %r" % (seq_id,))
+        if self.swapped[seq_id]:
+            raise AllocError(ERR_INVALID_ARG, "sequence %r is swapped out" % (seq_id,))
         tab = self.tables[seq_id]
         pos = self.lengths[seq_id]
         off = pos % self.block_size
@@ -123,24 +147,90 @@ class BlockAllocatorModel:
     def free_seq(self, seq_id):
         if seq_id not in self.tables:
             raise AllocError(ERR_UNKNOWN_SEQ, "unknown sequence %r" % (seq_id,))
+        refs, free = ((self.host_refcount, self.host_free) if self.swapped[seq_id]
+                      else (self.refcount, self.free))
         for b in reversed(self.tables[seq_id]):
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
+            refs[b] -= 1
+            if refs[b] == 0:
+                free.append(b)
         del self.tables[seq_id]
         del self.lengths[seq_id]
+        del self.swapped[seq_id]
+
+    # --- swapping ----------------------------------------------------------
+    def set_swap_space(self, num_host_blocks: int):
+        if num_host_blocks < 0:
+            raise AllocError(ERR_INVALID_ARG, "negative swap space")
+        if any(self.swapped.values()):
+            raise AllocError(ERR_INVALID_ARG, "a sequence is swapped out")
+        self.host_free = list(range(num_host_blocks - 1, -1, -1))   # pops 0, 1, 2, ...
+        self.host_refcount = [0] * num_host_blocks
+
+    def swap_out(self, seq_ids):
+        """Returns the (device block, swap block) pairs to copy."""
+        return self._move(list(seq_ids), to_host=True)
+
+    def swap_in(self, seq_ids):
+        """Returns the (swap block, device block) pairs to copy."""
+        return self._move(list(seq_ids), to_host=False)
+
+    def _move(self, seq_ids, to_host):
+        seen = set()
+        for sid in seq_ids:
+            if sid not in self.tables:
+                raise AllocError(ERR_UNKNOWN_SEQ, "unknown sequence %r" % (sid,))
+            if self.swapped[sid] == to_host:
+                raise AllocError(ERR_INVALID_ARG, "sequence %r already there" % (sid,))
+            if sid in seen:
+                raise AllocError(ERR_INVALID_ARG, "sequence %r given twice" % (sid,))
+            seen.add(sid)
+        uses = {}   # block -> references from the group, in order of first appearance
+        for sid in seq_ids:
+            for b in self.tables[sid]:
+                uses[b] = uses.get(b, 0) + 1
+        if to_host:
+            old_ref, old_free, new_ref, new_free = (self.refcount, self.free,
+                                                    self.host_refcount, self.host_free)
+        else:
+            old_ref, old_free, new_ref, new_free = (self.host_refcount, self.host_free,
+                                                    self.refcount, self.free)
+        if len(uses) > len(new_free):
+            raise AllocError(ERR_OUT_OF_BLOCKS, "target pool exhausted")
+        where, pairs = {}, []
+        for b, n in uses.items():
+            t = new_free.pop()
+            new_ref[t] = n
+            where[b] = t
+            pairs.append((b, t))
+        for b in reversed(list(uses)):
+            old_ref[b] -= uses[b]
+            if old_ref[b] == 0:
+                old_free.append(b)
+        for sid in seq_ids:
+            self.tables[sid] = [where[b] for b in self.tables[sid]]
+            self.swapped[sid] = to_host
+        return pairs
 
     # --- invariants --------------------------------------------------------
     def check_invariants(self):
         refs = [0] * self.num_blocks
-        for tab in self.tables.values():
+        host_refs = [0] * len(self.host_refcount)
+        for sid, tab in self.tables.items():
             for b in tab:
-                refs[b] += 1
+                if self.swapped[sid]:
+                    host_refs[b] += 1
+                else:
+                    refs[b] += 1
         assert refs == self.refcount, "refcounts disagree with the tables"
+        assert host_refs == self.host_refcount, "swap refcounts disagree with the tables"
         free = set(self.free)
         assert len(free) == len(self.free), "a block is on the free list twice"
         for b in range(self.num_blocks):
             assert (b in free) == (self.refcount[b] == 0), "block %d free/referenced mismatch" % b
+        hfree = set(self.host_free)
+        assert len(hfree) == len(self.host_free), "a swap block is on its free list twice"
+        for b in range(len(self.host_refcount)):
+            assert (b in hfree) == (self.host_refcount[b] == 0), "swap block %d mismatch" % b
         for sid, tab in self.tables.items():
             L = self.lengths[sid]
             assert len(tab) == -(-L // self.block_size), "table length disagrees with tokens"

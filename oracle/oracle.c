@@ -249,3 +249,29 @@ int oracle_copy_blocks(void *key_cache, void *value_cache, const int64_t *block_
   free(snap);
   return OR_OK;
 }
+
+/* swap_blocks: the copy of swapping a preempted sequence's blocks to host
+ * memory and back (inferensys glossary "Paged Attention", third and fifth
+ * paragraphs).  For each pair (s, t), block t of the destination pools
+ * becomes a copy of block s of the source pools: K and V, every head and
+ * slot.  The pools are distinct, so the order of the pairs does not matter. */
+int oracle_swap_blocks(void *dst_key, void *dst_value, const void *src_key,
+                       const void *src_value, const int64_t *block_mapping, int num_pairs,
+                       int num_kv_heads, int head_dim, int block_size, int64_t src_num_blocks,
+                       int64_t dst_num_blocks, int dtype) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      (dtype != OR_FP32 && dtype != OR_BF16))
+    return OR_ERR_ARG;
+  const size_t block_bytes = (size_t)num_kv_heads * head_dim * block_size * elem_size(dtype);
+  for (int p = 0; p < num_pairs; ++p) {
+    const int64_t s = block_mapping[2 * p], t = block_mapping[2 * p + 1];
+    if (s < 0 || s >= src_num_blocks || t < 0 || t >= dst_num_blocks) return OR_ERR_ARG;
+  }
+  for (int p = 0; p < num_pairs; ++p) {
+    const int64_t s = block_mapping[2 * p], t = block_mapping[2 * p + 1];
+    memcpy((char *)dst_key + t * block_bytes, (const char *)src_key + s * block_bytes, block_bytes);
+    memcpy((char *)dst_value + t * block_bytes, (const char *)src_value + s * block_bytes,
+           block_bytes);
+  }
+  return OR_OK;
+}

@@ -8,7 +8,9 @@ Python binding:
     per-sequence block tables (HIP kernels; MFMA for grouped-query heads);
   * ``reshape_and_cache`` -- write new tokens' K/V into their slots;
   * ``copy_blocks`` -- the copy of copy-on-write;
-  * ``BlockAllocator`` -- host free list, refcounts and copy-on-write.
+  * ``swap_blocks`` -- block copies between GPU and pinned host pools;
+  * ``BlockAllocator`` -- host free list, refcounts, copy-on-write and a
+    swap space for preempted sequences.
 """
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARG, PA_ERR_OUT_OF_BLOCKS,
@@ -16,4 +18,4 @@ from ._binding import (  # noqa: F401
     PA_PARTITION_BALANCED, BlockAllocator, PagedAttnError,
     allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
     paged_attention_workspace_bytes, reshape_and_cache, set_balance_weights, set_timing_events,
-    value_cache_shape)
+    swap_blocks, value_cache_shape)

@@ -35,11 +35,12 @@ EXPORTS = (
     "pa_paged_attention_decode", "pa_paged_attention_decode_append",
     "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
     "pa_set_balance_weights",
-    "pa_reshape_and_cache", "pa_copy_blocks",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks",
     "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free",
     "pa_allocator_block_size", "pa_seq_create", "pa_seq_fork", "pa_seq_append_slot",
     "pa_seq_free", "pa_seq_block_table", "pa_seq_len", "pa_block_refcount",
-    "pa_build_block_tables",
+    "pa_build_block_tables", "pa_allocator_set_swap_space", "pa_allocator_num_free_host",
+    "pa_host_block_refcount", "pa_seq_is_swapped", "pa_seqs_swap_out", "pa_seqs_swap_in",
 )
 
 
@@ -70,6 +71,13 @@ def _declare(lib):
         "pa_set_balance_weights": (i32, [vp, i32]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
+        "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32, vp]),
+        "pa_allocator_set_swap_space": (i32, [vp, i64]),
+        "pa_allocator_num_free_host": (i64, [vp]),
+        "pa_host_block_refcount": (i32, [vp, i32]),
+        "pa_seq_is_swapped": (i32, [vp, i64]),
+        "pa_seqs_swap_out": (i32, [vp, vp, i32, vp, i32, p_i32]),
+        "pa_seqs_swap_in": (i32, [vp, vp, i32, vp, i32, p_i32]),
         "pa_allocator_create": (vp, [i64, i32, vp]),
         "pa_allocator_destroy": (None, [vp]),
         "pa_allocator_num_free": (i64, [vp]),
@@ -329,6 +337,36 @@ def copy_blocks(key_cache, value_cache, block_mapping, *, num_kv_heads: int, hea
         _dtype_code(key_cache), _stream(dev, stream)))
 
 
+def swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, block_mapping,
+                *, num_kv_heads: int, head_dim: int, block_size: int, stream=None):
+    """Copy whole blocks (src block, dst block) = block_mapping[k] from the src
+    pools to the dst pools.  Each pool, and block_mapping (int64 [n, 2]), is
+    either on the GPU or in pinned host memory (pin_memory=True)."""
+    lib = load()
+    torch = _torch()
+    tensors = ((dst_key_cache, "dst_key_cache"), (dst_value_cache, "dst_value_cache"),
+               (src_key_cache, "src_key_cache"), (src_value_cache, "src_value_cache"),
+               (block_mapping, "block_mapping"))
+    devs = {t.device for t, _ in tensors if t.is_cuda}
+    if len(devs) != 1:
+        raise ValueError("swap_blocks needs tensors on exactly one GPU (the others pinned)")
+    dev = devs.pop()
+    for t, n in tensors:
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError("%s must be on the GPU or in pinned host memory" % n)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    if block_mapping.dtype != torch.int64 or block_mapping.numel() % 2:
+        raise ValueError("block_mapping must be int64 [num_pairs, 2]")
+    if dst_key_cache.dtype != src_key_cache.dtype:
+        raise TypeError("pools must share a dtype")
+    _check(lib.pa_swap_blocks(
+        dst_key_cache.data_ptr(), dst_value_cache.data_ptr(), src_key_cache.data_ptr(),
+        src_value_cache.data_ptr(), block_mapping.data_ptr(), block_mapping.numel() // 2,
+        num_kv_heads, head_dim, block_size, int(src_key_cache.shape[0]),
+        int(dst_key_cache.shape[0]), _dtype_code(src_key_cache), _stream(dev, stream)))
+
+
 # ---- allocator -----------------------------------------------------------------
 
 class BlockAllocator:
@@ -393,6 +431,41 @@ class BlockAllocator:
         _check(self._lib.pa_seq_block_table(self._h, int(seq_id), buf.ctypes.data, cap,
                                             ctypes.byref(n)))
         return buf[:n.value].tolist()
+
+    def set_swap_space(self, num_host_blocks: int):
+        _check(self._lib.pa_allocator_set_swap_space(self._h, int(num_host_blocks)))
+
+    def num_free_host(self) -> int:
+        return int(self._lib.pa_allocator_num_free_host(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return int(self._lib.pa_host_block_refcount(self._h, int(block)))
+
+    def is_swapped(self, seq_id: int) -> bool:
+        r = int(self._lib.pa_seq_is_swapped(self._h, int(seq_id)))
+        if r < 0:
+            raise _err(PA_ERR_UNKNOWN_SEQ)
+        return bool(r)
+
+    def _swap(self, fn, seq_ids):
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        cap = 0
+        for i in ids.tolist():
+            cap += -(-max(self.seq_len(i), 0) // self.block_size)
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int64)
+        n = ctypes.c_int32()
+        _check(fn(self._h, ids.ctypes.data, int(ids.shape[0]), pairs.ctypes.data, cap,
+                  ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_ids):
+        """Preempt these sequences to the swap space; returns int64 [n, 2]
+        (device block, swap block) pairs to copy with swap_blocks."""
+        return self._swap(self._lib.pa_seqs_swap_out, seq_ids)
+
+    def swap_in(self, seq_ids):
+        """Bring swapped sequences back; returns (swap block, device block) pairs."""
+        return self._swap(self._lib.pa_seqs_swap_in, seq_ids)
 
     def build_block_tables(self, seq_ids, max_blocks: int, pad: int = 0):
         """Host int32 tables [n, max_blocks] (padded) and lengths [n] for upload."""

@@ -31,9 +31,23 @@ pa_status to_host(std::vector<T> &dst, const T *src, size_t n, void *stream) {
   dst.resize(n);
   if (n == 0) return PA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  // hipMemcpyDefault: src may be device memory or pinned host memory.
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? PA_OK : hip_fail("PA_VALIDATE copy", (int)e);
+}
+
+// True when the device can read and write p directly: device memory, or
+// pinned host memory mapped at the same address (hipHostMalloc on ROCm).
+// Pageable host memory -- which a kernel access would fault on -- is refused.
+bool device_addressable(const void *p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the error the query leaves behind
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice) return true;
+  return at.type == hipMemoryTypeHost && at.devicePointer == p;
 }
 
 void *g_ev_before_main = nullptr;
@@ -397,8 +411,59 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int64_t *bloc
         return pa_fail(PA_ERR_INVALID_ARG, "%s: block %lld is both a source and a destination",
                        fn, (long long)d);
   }
-  const int e = pa::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
-                                       block_bytes, num_blocks, stream);
+  const int e = pa::launch_copy_blocks(key_cache, value_cache, key_cache, value_cache,
+                                       block_mapping, num_pairs, block_bytes, num_blocks,
+                                       num_blocks, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+pa_status pa_swap_blocks(void *dst_key_cache, void *dst_value_cache, const void *src_key_cache,
+                         const void *src_value_cache, const int64_t *block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t src_num_blocks, int64_t dst_num_blocks,
+                         pa_dtype dtype, void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_swap_blocks";
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_FP32 or PA_BF16", fn);
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: sizes must be positive (num_pairs >= 0)", fn);
+  const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * esz;
+  if (block_bytes % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block bytes must be a multiple of 16", fn);
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !block_mapping)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned16(dst_key_cache) || !aligned16(dst_value_cache) || !aligned16(src_key_cache) ||
+      !aligned16(src_value_cache))
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: pools must be 16-byte aligned", fn);
+  const void *ptrs[5] = {dst_key_cache, dst_value_cache, src_key_cache, src_value_cache,
+                         block_mapping};
+  const char *names[5] = {"dst_key_cache", "dst_value_cache", "src_key_cache",
+                          "src_value_cache", "block_mapping"};
+  for (int i = 0; i < 5; ++i)
+    if (!device_addressable(ptrs[i]))
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: %s is neither device memory nor pinned host "
+                     "memory the device can address", fn, names[i]);
+  if (deep_validation()) {
+    std::vector<int64_t> m;
+    pa_status s = to_host(m, block_mapping, (size_t)num_pairs * 2, stream);
+    if (s != PA_OK) return s;
+    std::unordered_set<int64_t> dsts;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      if (m[2 * i] < 0 || m[2 * i] >= src_num_blocks || m[2 * i + 1] < 0 ||
+          m[2 * i + 1] >= dst_num_blocks)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: pair %d = (%lld, %lld) outside the pools", fn,
+                       i, (long long)m[2 * i], (long long)m[2 * i + 1]);
+      if (!dsts.insert(m[2 * i + 1]).second)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: destination %lld repeats", fn,
+                       (long long)m[2 * i + 1]);
+    }
+  }
+  const int e = pa::launch_copy_blocks(dst_key_cache, dst_value_cache, src_key_cache,
+                                       src_value_cache, block_mapping, num_pairs, block_bytes,
+                                       src_num_blocks, dst_num_blocks, stream);
   return e == 0 ? PA_OK : hip_fail(fn, e);
 }
 

@@ -7,6 +7,9 @@
 //  * copy_blocks: the copy half of copy-on-write, giving a writer its own
 //    copy of a shared block (note-023, "Concepts"; inferensys glossary,
 //    second paragraph).  Whole blocks: K and V, all heads, all slots.
+//  * swap_blocks: the same copy between two pools (device and pinned host
+//    memory), for swapping preempted sequences out and back in (inferensys
+//    glossary, third and fifth paragraphs).
 //
 // Both are bit copies.  Pool layout, x = 16 / element size:
 //   key   [num_blocks][Hkv][d / x][block_size][x]
@@ -61,18 +64,21 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// Grid: x = 16-byte pieces of a block, y = pair, z = pool (0 key, 1 value).
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char *__restrict__ key_cache,
-                                                          char *__restrict__ value_cache,
-                                                          const int64_t *__restrict__ pairs,
-                                                          int64_t block_bytes,
-                                                          int64_t num_blocks) {
+// Whole-block copies from (src_key, src_value) to (dst_key, dst_value); the
+// pools may be the same (copy_blocks) or different, device or pinned host
+// (swap_blocks).  Grid: x = 16-byte pieces of a block, y = pair, z = pool
+// (0 key, 1 value).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    char *dst_key, char *dst_value, const char *src_key, const char *src_value,
+    const int64_t *__restrict__ pairs, int64_t block_bytes, int64_t src_blocks,
+    int64_t dst_blocks) {
   const int64_t src = pairs[2 * (int64_t)blockIdx.y];
   const int64_t dst = pairs[2 * (int64_t)blockIdx.y + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  char *pool = blockIdx.z == 0 ? key_cache : value_cache;
-  const u32x4 *s = reinterpret_cast<const u32x4 *>(pool + src * block_bytes);
-  u32x4 *d = reinterpret_cast<u32x4 *>(pool + dst * block_bytes);
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const char *sp = blockIdx.z == 0 ? src_key : src_value;
+  char *dp = blockIdx.z == 0 ? dst_key : dst_value;
+  const u32x4 *s = reinterpret_cast<const u32x4 *>(sp + src * block_bytes);
+  u32x4 *d = reinterpret_cast<u32x4 *>(dp + dst * block_bytes);
   const int64_t n = block_bytes / 16;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -105,8 +111,10 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
   return (int)hipGetLastError();
 }
 
-int launch_copy_blocks(void *key_cache, void *value_cache, const int64_t *pairs,
-                       int32_t num_pairs, int64_t block_bytes, int64_t num_blocks, void *stream) {
+int launch_copy_blocks(void *dst_key, void *dst_value, const void *src_key,
+                       const void *src_value, const int64_t *pairs, int32_t num_pairs,
+                       int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
+                       void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t pieces = block_bytes / 16;
   const int64_t gx64 = (pieces + 255) / 256;
@@ -115,8 +123,9 @@ int launch_copy_blocks(void *key_cache, void *value_cache, const int64_t *pairs,
   for (int32_t first = 0; first < num_pairs; first += 65535) {
     const int32_t n = num_pairs - first < 65535 ? num_pairs - first : 65535;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)n, 2), dim3(256), 0, st,
-                       static_cast<char *>(key_cache), static_cast<char *>(value_cache),
-                       pairs + 2 * (int64_t)first, block_bytes, num_blocks);
+                       static_cast<char *>(dst_key), static_cast<char *>(dst_value),
+                       static_cast<const char *>(src_key), static_cast<const char *>(src_value),
+                       pairs + 2 * (int64_t)first, block_bytes, src_blocks, dst_blocks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }

@@ -155,22 +155,28 @@ def test_failures_leave_state_unchanged():
 
 
 def random_trace(seed, n_ops=400, num_blocks=64, block_size=4):
-    """A seeded op list over create/fork/append/free (also used against the C++ allocator)."""
+    """A seeded op list over create/fork/append/free and group swaps out and
+    in (also used against the C++ allocator).  Ops on swapped or unknown
+    sequences are included on purpose: they must fail the same way."""
     rng = np.random.default_rng(seed)
-    ops, live, next_id = [], [], 0
+    ops, live, next_id = [("swap_space", num_blocks // 2)], [], 0
     for _ in range(n_ops):
         r = rng.random()
-        if r < 0.2 or not live:
+        if r < 0.18 or not live:
             ops.append(("create", next_id, int(rng.integers(0, 3 * block_size + 1))))
             live.append(next_id); next_id += 1
-        elif r < 0.35:
+        elif r < 0.32:
             ops.append(("fork", int(rng.choice(live)), next_id))
             live.append(next_id); next_id += 1
-        elif r < 0.85:
+        elif r < 0.76:
             ops.append(("append", int(rng.choice(live))))
-        else:
+        elif r < 0.86:
             s = int(rng.choice(live)); live.remove(s)
             ops.append(("free", s))
+        else:
+            k = int(rng.integers(1, min(4, len(live)) + 1))
+            group = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            ops.append(("swap_out" if rng.random() < 0.5 else "swap_in", group))
         if rng.random() < 0.03:
             ops.append(("free", 10 ** 6))           # unknown id
     return ops
@@ -184,6 +190,12 @@ def apply_model(a, op):
             a.fork(op[1], op[2]); return (0,)
         if op[0] == "append":
             return (0,) + a.append_slot(op[1])
+        if op[0] == "swap_space":
+            a.set_swap_space(op[1]); return (0,)
+        if op[0] == "swap_out":
+            return (0, tuple(a.swap_out(op[1])))
+        if op[0] == "swap_in":
+            return (0, tuple(a.swap_in(op[1])))
         a.free_seq(op[1]); return (0,)
     except AllocError as e:
         return (e.code,)
@@ -196,9 +208,95 @@ def test_invariants_hold_after_every_operation(seed):
     for op in random_trace(seed):
         r = apply_model(a, op)
         a.check_invariants()
+        if op[0] in ("swap_out", "swap_in") and r[0] == 0:
+            # Every moved block went to a distinct block of the other pool.
+            dsts = [t for _, t in r[1]]
+            assert len(set(dsts)) == len(dsts)
+            assert all(a.swapped[sid] == (op[0] == "swap_out") for sid in op[1])
         if op[0] == "append" and r[0] == 0:
             slot, src, dst = r[1:]
             # After an append the written block belongs to this sequence alone.
             assert a.refcount[a.table(op[1])[-1]] == 1
             assert slot // 4 == a.table(op[1])[-1]
             assert (src == -1) == (dst == -1)
+
+
+# ---- swapping (inferensys glossary, third and fifth paragraphs) -------------
+
+def _group():
+    """Prompt 0 of 10 tokens (3 blocks of 4), child 1 forked from it and
+    grown by 3 tokens (copy of the shared partial block, then a new block)."""
+    a = BlockAllocatorModel(16, 4)
+    a.set_swap_space(8)
+    a.create(0, 10)
+    a.fork(0, 1)
+    for _ in range(3):
+        a.append_slot(1)
+    return a
+
+
+def test_swapping_a_group_moves_each_distinct_block_once():
+    a = _group()
+    assert a.table(0) == [0, 1, 2] and a.table(1) == [0, 1, 3, 4]
+    pairs = a.swap_out([0, 1])
+    # Distinct blocks in first-appearance order, swap blocks popped 0, 1, 2, ...
+    assert pairs == [(0, 0), (1, 1), (2, 2), (3, 3), (4, 4)]
+    assert a.host_refcount[:5] == [2, 2, 1, 1, 1]
+    assert a.table(0) == [0, 1, 2] and a.table(1) == [0, 1, 3, 4]     # now swap-space ids
+    assert a.num_free() == 16 and all(r == 0 for r in a.refcount)
+    # Freed in reverse order of first appearance: block 0 is handed out next.
+    assert a.free[-5:] == [4, 3, 2, 1, 0]
+    a.check_invariants()
+
+
+def test_a_sharer_left_behind_keeps_the_original():
+    a = _group()
+    pairs = a.swap_out([1])
+    assert [b for b, _ in pairs] == [0, 1, 3, 4]
+    assert a.refcount[0] == 1 and a.refcount[1] == 1      # still held by sequence 0
+    assert a.refcount[3] == 0 and a.refcount[4] == 0
+    a.check_invariants()
+
+
+def test_swap_round_trip_resumes_where_it_stopped():
+    a = _group()
+    lens = (a.length(0), a.length(1))
+    a.swap_out([0, 1])
+    a.create(5, 12)                                       # someone else takes the blocks
+    pairs = a.swap_in([1, 0])
+    assert (a.length(0), a.length(1)) == lens
+    # Sharing inside the group survives: the two prefixes are one set of blocks.
+    assert a.table(0)[:2] == a.table(1)[:2]
+    assert a.refcount[a.table(0)[0]] == 2
+    assert sorted(a.table(0) + a.table(1)[2:]) == sorted(t for _, t in pairs)
+    slot, src, dst = a.append_slot(1)                     # next position, same offset rule
+    assert slot % 4 == lens[1] % 4 and src == -1
+    a.check_invariants()
+
+
+def test_swapped_sequences_refuse_growth_and_failed_swaps_change_nothing():
+    a = _group()
+    a.swap_out([1])
+    for fn, code in [(lambda: a.append_slot(1), ERR_INVALID_ARG),
+                     (lambda: a.fork(1, 9), ERR_INVALID_ARG),
+                     (lambda: a.swap_out([1]), ERR_INVALID_ARG),
+                     (lambda: a.swap_in([0]), ERR_INVALID_ARG),
+                     (lambda: a.swap_out([0, 0]), ERR_INVALID_ARG),
+                     (lambda: a.swap_in([7]), ERR_UNKNOWN_SEQ),
+                     (lambda: a.set_swap_space(4), ERR_INVALID_ARG)]:
+        snap = (list(a.free), list(a.refcount), list(a.host_free), list(a.host_refcount),
+                {k: list(v) for k, v in a.tables.items()}, dict(a.swapped))
+        with pytest.raises(AllocError) as e:
+            fn()
+        assert e.value.code == code
+        assert snap == (list(a.free), list(a.refcount), list(a.host_free),
+                        list(a.host_refcount), {k: list(v) for k, v in a.tables.items()},
+                        dict(a.swapped))
+    # The swap space has 4 free blocks left; sequence 0's 3 fit, a bigger group does not.
+    a.create(3, 16)
+    with pytest.raises(AllocError) as e:
+        a.swap_out([0, 3])
+    assert e.value.code == ERR_OUT_OF_BLOCKS
+    a.free_seq(1)                                         # releases its swap blocks
+    assert a.host_refcount == [0] * 8 and len(a.host_free) == 8
+    a.check_invariants()

@@ -22,30 +22,30 @@ def apply_cpp(a, op):
             a.fork(op[1], op[2]); return (0,)
         if op[0] == "append":
             return (0,) + a.append_slot(op[1])
+        if op[0] == "swap_space":
+            a.set_swap_space(op[1]); return (0,)
+        if op[0] == "swap_out":
+            return (0, tuple(map(tuple, a.swap_out(op[1]).tolist())))
+        if op[0] == "swap_in":
+            return (0, tuple(map(tuple, a.swap_in(op[1]).tolist())))
         a.free(op[1]); return (0,)
     except pa.PagedAttnError as e:
         return (e.status,)
 
 
-def apply_model(a, op):
-    try:
-        if op[0] == "create":
-            a.create(op[1], op[2]); return (0,)
-        if op[0] == "fork":
-            a.fork(op[1], op[2]); return (0,)
-        if op[0] == "append":
-            return (0,) + a.append_slot(op[1])
-        a.free_seq(op[1]); return (0,)
-    except AllocError as e:
-        return (e.code,)
+from tests.test_alloc_model import apply_model  # noqa: E402
 
 
 def same_state(cpp, model):
     assert cpp.num_free() == model.num_free()
     assert [cpp.refcount(b) for b in range(model.num_blocks)] == model.refcount
+    assert cpp.num_free_host() == len(model.host_free)
+    assert [cpp.host_refcount(b) for b in range(len(model.host_refcount))] == \
+        model.host_refcount
     for sid, tab in model.tables.items():
         assert cpp.block_table(sid) == tab
         assert cpp.seq_len(sid) == model.lengths[sid]
+        assert cpp.is_swapped(sid) == model.swapped[sid]
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -55,12 +55,14 @@ def test_cpp_allocator_matches_model_on_random_traces(seed, nblocks, bs):
     cpp = pa.BlockAllocator(nblocks, bs, order if seed % 2 else None)
     model = BlockAllocatorModel(nblocks, bs, order if seed % 2 else None)
     ops = random_trace(seed, n_ops=500, num_blocks=nblocks, block_size=bs)
-    saw_oom = False
+    saw_oom, swaps = False, 0
     for op in ops:
         r1, r2 = apply_cpp(cpp, op), apply_model(model, op)
         assert r1 == r2, (op, r1, r2)
         saw_oom |= r1[0] == pa.PA_ERR_OUT_OF_BLOCKS
+        swaps += op[0].startswith("swap_") and r1[0] == 0
         same_state(cpp, model)
+    assert swaps > 0
     # The next hand-outs come in the same order (free lists agree as stacks).
     k = 0
     while model.num_free():

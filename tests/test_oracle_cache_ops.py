@@ -107,3 +107,49 @@ def test_bf16_bits_survive_the_scatter_unchanged():
                              head_dim=8, block_size=16, num_blocks=1)
     assert np.array_equal(kp[0, 0, 0, 3], key[0, 0])
     assert np.array_equal(vp[0, 0, :, 3], key[0, 0])
+
+
+# ---- swap_blocks (inferensys glossary, third and fifth paragraphs) -----------
+
+def test_swap_out_and_back_in_restores_every_token_of_the_swapped_blocks():
+    """Device pool -> swap pool -> a different device block: the gathered
+    tokens of each moved block are unchanged, the rest of both pools too."""
+    rng = np.random.default_rng(35)
+    N, H, Hkv, d, Bs = 10, 6, 2, 64, 16
+    bits = lambda shape: rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    kp, vp = bits((N, Hkv, d // 8, Bs, 8)), bits((N, Hkv, d, Bs))
+    hk, hv = bits((H, Hkv, d // 8, Bs, 8)), bits((H, Hkv, d, Bs))
+    k0, v0, hk0, hv0 = kp.copy(), vp.copy(), hk.copy(), hv.copy()
+    out = np.array([[7, 0], [2, 5], [4, 1]], np.int64)          # device -> swap
+    oracle.swap_blocks(hk, hv, kp, vp, out, num_kv_heads=Hkv, head_dim=d, block_size=Bs)
+    back = np.array([[0, 3], [5, 9], [1, 8]], np.int64)         # swap -> new device blocks
+    oracle.swap_blocks(kp, vp, hk, hv, back, num_kv_heads=Hkv, head_dim=d, block_size=Bs)
+    for (dev, swp), (swp2, new) in zip(out, back):
+        assert swp == swp2
+        got = pl.gather_sequence(kp, vp, [new], Bs, Bs)
+        want = pl.gather_sequence(k0, v0, [dev], Bs, Bs)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    untouched_dev = [b for b in range(N) if b not in (3, 9, 8)]
+    assert np.array_equal(kp[untouched_dev], k0[untouched_dev])
+    assert np.array_equal(hk[[2, 3, 4]], hk0[[2, 3, 4]]) and np.array_equal(hv[[2, 3]], hv0[[2, 3]])
+
+
+def test_swap_within_one_pool_equals_copy_blocks():
+    rng = np.random.default_rng(36)
+    kp = rng.standard_normal((8, 2, 8, 32, 4)).astype(np.float32)
+    vp = rng.standard_normal((8, 2, 32, 32)).astype(np.float32)
+    pairs = np.array([[1, 4], [1, 6], [3, 0]], np.int64)
+    a_k, a_v = kp.copy(), vp.copy()
+    oracle.copy_blocks(a_k, a_v, pairs, num_kv_heads=2, head_dim=32, block_size=32, num_blocks=8)
+    b_k, b_v = kp.copy(), vp.copy()
+    oracle.swap_blocks(b_k, b_v, kp, vp, pairs, num_kv_heads=2, head_dim=32, block_size=32)
+    assert np.array_equal(a_k, b_k) and np.array_equal(a_v, b_v)
+
+
+def test_swap_rejects_blocks_outside_either_pool():
+    kp, vp = pl.empty_pools(4, 1, 16, 16, np.float32)
+    hk, hv = pl.empty_pools(2, 1, 16, 16, np.float32)
+    for bad in ([[4, 0]], [[0, 2]], [[-1, 0]]):
+        with pytest.raises(ValueError):
+            oracle.swap_blocks(hk, hv, kp, vp, np.array(bad, np.int64), num_kv_heads=1,
+                               head_dim=16, block_size=16)
