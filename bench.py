@@ -56,22 +56,32 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def build_step(name, ps, device):
+def build_step(name, ps, device, block_size=None, table_order="random"):
     import workloads as W
     from paged_kv_cache_305_amd.step import shared_prefix_step, step_from_case
     if name == "shared":
-        plan = W.shared_plan()
+        if table_order != "random":
+            raise SystemExit("the shared-prefix tables come from the allocator")
+        plan = W.shared_plan(block_size=block_size)
         tens = W.shared_tensors(plan, device=device)
         step, rec = shared_prefix_step(plan, tens, partition_size=ps)
         lens = rec["lens"].astype(np.int64)
         return step, lens, dict(seed=plan.seed, cow_pairs=int(rec["pairs"].shape[0]),
-                                num_blocks=plan.num_blocks)
+                                num_blocks=plan.num_blocks, block_size=plan.block_size)
     base = "long" if name == "long32" else name
-    kw = dict(block_size=32) if name == "long32" else {}
-    case = W.make_case(base, device=device, **kw)
+    bs = block_size or (32 if name == "long32" else None)
+    case = W.make_case(base, device=device, **(dict(block_size=bs) if bs else {}))
+    if table_order == "identity":
+        # Contiguous storage: each sequence's blocks are consecutive physical
+        # blocks, sequences one after another.
+        case.block_tables = W.tables_from_perm(case.context_lens,
+                                               np.arange(case.num_blocks, dtype=np.int32),
+                                               case.block_size)
+        case.slot_mapping = W.slots_at(case.context_lens, case.block_tables, case.block_size)
     step = step_from_case(case, partition_size=ps)
-    return step, case.context_lens.astype(np.int64), dict(seed=case.seed,
-                                                          num_blocks=case.num_blocks)
+    return step, case.context_lens.astype(np.int64), dict(
+        seed=case.seed, num_blocks=case.num_blocks, block_size=case.block_size,
+        table_order=table_order)
 
 
 def unique_kv_tokens(step, lens):
@@ -102,6 +112,49 @@ def block_waste(step, lens):
     allocated = len(blocks) * step.block_size
     return dict(kv_slots_allocated=allocated, kv_slots_used=used,
                 kv_block_waste_frac=round(1.0 - used / allocated, 5) if allocated else 0.0)
+
+
+# Longest context each workload reserves when storage is one contiguous
+# max-length region per sequence (the prior allocation scheme the pages
+# compare against): the upper end of its length distribution.
+MAX_CONTEXT = {"7b": 2048, "70b": 4096, "long": 32768, "shared": 4000 + 512 + 1}
+
+
+def waste_report(block_sizes=(8, 16, 32, 64)):
+    """KV-cache internal waste of each workload's step through the block
+    allocator, per block size, next to contiguous max-length reservation
+    (note-023 Key results and Concepts; inferensys glossary, first
+    paragraph; crackai.dev, Why It Matters).  Host only."""
+    import workloads as W
+    import paged_kv_cache_305_amd as pa
+    from paged_kv_cache_305_amd.step import build_shared_prefix_state
+    rows = []
+    for name in ("7b", "70b", "shared", "long"):
+        for bs in block_sizes:
+            if name == "shared":
+                plan = W.shared_plan(block_size=bs)
+                a = build_shared_prefix_state(plan)
+                lens = [plan.prompt + int(t) for t in plan.tails]
+                used = plan.prompt + int(sum(plan.tails))          # distinct tokens stored
+                total = plan.num_blocks
+            else:
+                st = W.case_structure(name, block_size=bs)
+                lens = [int(L) for L in st.lengths]
+                total = int(sum(-(-L // bs) for L in lens))
+                a = pa.BlockAllocator(total, bs)
+                for i, L in enumerate(lens):
+                    a.create(i, L)
+                used = int(sum(lens))
+            allocated = (total - a.num_free()) * bs
+            reserved = len(lens) * MAX_CONTEXT[name]
+            rows.append(dict(workload=name, block_size=bs, sequences=len(lens),
+                             tokens_used=used, slots_allocated=allocated,
+                             paged_waste=round(1 - used / allocated, 5),
+                             contiguous_reserved_slots=reserved,
+                             contiguous_waste=round(1 - sum(lens) / reserved, 5),
+                             paged_over_contiguous_memory=round(allocated / reserved, 5)))
+            a.close()
+    return rows
 
 
 def cpu_model():
@@ -276,6 +329,13 @@ def main():
                          "reshape_and_cache before it (separate), or by batch size (auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="block size of the workload (default: the workload's own)")
+    ap.add_argument("--table-order", choices=["random", "identity"], default="random",
+                    help="physical blocks in random order (paged) or consecutive (contiguous)")
+    ap.add_argument("--waste-report", action="store_true",
+                    help="only print the allocator's KV waste per workload and block size "
+                         "(host only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -288,6 +348,10 @@ def main():
 
     import torch
     import paged_kv_cache_305_amd as pa
+    if args.waste_report:
+        for row in waste_report():
+            print(json.dumps(row), flush=True)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -302,7 +366,8 @@ def main():
         return
 
     log("building workload %s" % args.workload)
-    step, lens, info = build_step(args.workload, args.partition_size, device)
+    step, lens, info = build_step(args.workload, args.partition_size, device,
+                                  block_size=args.block_size, table_order=args.table_order)
     step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)

@@ -26,11 +26,12 @@
  *
  * Pool layout (one layer; K and V in separate pools), x = 16 / element size:
  *    key   pool [num_blocks][num_kv_heads][head_dim / x][block_size][x]
- *    value pool [num_blocks][num_kv_heads][head_dim][block_size]
+ *    value pool [num_blocks][num_kv_heads][block_size / 16][head_dim][16]
  *  so every (block, KV head) chunk is block_size * head_dim contiguous
  *  elements; keys keep 16-byte runs of one token's features, values keep
- *  each feature's block_size tokens together.  A slot is
- *  physical_block * block_size + offset_in_block.
+ *  each feature's tokens together in groups of 16 (one group per 16-token
+ *  tile the kernels read).  A slot is physical_block * block_size +
+ *  offset_in_block.
  *
  * Allocator handles are library-owned host objects, not thread-safe, and
  * destroyed by the caller.
@@ -111,7 +112,7 @@ int32_t pa_version(void);
  *  workspace      device scratch of at least
  *                 pa_paged_attention_workspace_bytes(...) bytes when that is
  *                 nonzero (caller-owned, contents need not be initialised).
- *  Supported: head_dim in {64, 128}, block_size in {16, 32},
+ *  Supported: head_dim in {64, 128}, block_size in {16, 32, 64},
  *  kv_dtype/out_dtype in {PA_FP32, PA_BF16}; anything else returns
  *  PA_ERR_UNSUPPORTED.  bf16 outputs are rounded to nearest even.
  * ---------------------------------------------------------------------- */

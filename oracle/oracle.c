@@ -33,10 +33,12 @@
  * Pool layout (the library's, stated here so the oracle can address it):
  *   x = 16 / element size (4 for fp32, 8 for bf16)
  *   key   pool [num_blocks][Hkv][d / x][Bs][x]
- *   value pool [num_blocks][Hkv][d][Bs]
+ *   T = 16 when Bs is a multiple of 16, else T = Bs (values kept in
+ *       groups of T tokens)
+ *   value pool [num_blocks][Hkv][Bs/T][d][T]
  *   token o of block b, KV head g, feature e is
  *     key   (((b*Hkv + g)*(d/x) + e/x)*Bs + o)*x + e%x
- *     value ((b*Hkv + g)*d + e)*Bs + o
+ *     value (((b*Hkv + g)*(Bs/T) + o/T)*d + e)*T + o%T
  *
  * bf16 values are passed as raw uint16 bits and widened exactly
  * (bits << 16 is the fp32 value; fp32 -> fp64 is exact).
@@ -75,7 +77,8 @@ static int64_t key_index(int64_t b, int64_t g, int64_t o, int64_t e, int64_t hkv
 
 static int64_t value_index(int64_t b, int64_t g, int64_t o, int64_t e, int64_t hkv,
                            int64_t d, int64_t bs) {
-  return ((b * hkv + g) * d + e) * bs + o;
+  const int64_t t = bs % 16 == 0 ? 16 : bs;
+  return (((b * hkv + g) * (bs / t) + o / t) * d + e) * t + o % t;
 }
 
 typedef struct {

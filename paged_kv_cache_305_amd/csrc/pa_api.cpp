@@ -181,8 +181,9 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
     return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtypes must be PA_FP32 or PA_BF16", fn);
   if (head_dim != 64 && head_dim != 128)
     return pa_fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, head_dim);
-  if (block_size != 16 && block_size != 32)
-    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32)", fn, block_size);
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16, 32, 64)", fn,
+                   block_size);
   if (max_blocks_per_seq <= 0 || num_blocks <= 0)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq and num_blocks must be positive",
                    fn);

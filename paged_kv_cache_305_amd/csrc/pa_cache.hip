@@ -11,9 +11,10 @@
 //    memory), for swapping preempted sequences out and back in (inferensys
 //    glossary, third and fifth paragraphs).
 //
-// Both are bit copies.  Pool layout, x = 16 / element size:
+// Both are bit copies.  Pool layout, x = 16 / element size (block_size a
+// multiple of 16):
 //   key   [num_blocks][Hkv][d / x][block_size][x]
-//   value [num_blocks][Hkv][d][block_size]
+//   value [num_blocks][Hkv][block_size / 16][d][16]
 // Indices read from device memory (slots, pairs) are range-checked before
 // use; out-of-range entries are skipped so a bad input can never fault.
 #include <hip/hip_runtime.h>
@@ -27,7 +28,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // One thread per (token, KV head, 16-byte feature chunk).  The key chunk is
 // one 16-byte store (keys keep x features of a token together); the value
-// chunk scatters to x rows of the [d][block_size] value slab.
+// chunk scatters to x rows of the token's [d][16] value group.
 template <int ESZ>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char *__restrict__ key, const char *__restrict__ value, char *__restrict__ key_cache,
@@ -51,14 +52,16 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   *reinterpret_cast<u32x4 *>(key_cache + (head_base + ((int64_t)c * block_size + o) * X) * ESZ) =
       kv;
   const u32x4 vv = *reinterpret_cast<const u32x4 *>(value + src);
-  char *vdst = value_cache + (head_base + (int64_t)c * X * block_size + o) * ESZ;
+  char *vdst =
+      value_cache +
+      (head_base + (int64_t)(o / 16) * head_dim * 16 + (int64_t)c * X * 16 + o % 16) * ESZ;
 #pragma unroll
   for (int e = 0; e < X; ++e) {
     if (ESZ == 4) {
-      *reinterpret_cast<unsigned *>(vdst + (int64_t)e * block_size * ESZ) = vv[e];
+      *reinterpret_cast<unsigned *>(vdst + (int64_t)e * 16 * ESZ) = vv[e];
     } else {
       const unsigned w = vv[e >> 1];
-      *reinterpret_cast<uint16_t *>(vdst + (int64_t)e * block_size * ESZ) =
+      *reinterpret_cast<uint16_t *>(vdst + (int64_t)e * 16 * ESZ) =
           (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
     }
   }

@@ -419,7 +419,7 @@ __device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (
 // Lane l = 16*g + t.  Keys: for each tile, lane l loads the 16-byte key
 // chunks c = 4j + g (j < KJ) of token t; dot products are summed over the
 // lane's chunks, then across g with two cross-row exchanges, leaving token
-// t's logit in lanes t, t+16, t+32, t+48.  Values ([d][Bs] rows): lane l
+// t's logit in lanes t, t+16, t+32, t+48.  Values ([d][16] rows): lane l
 // loads 16-byte row segments (rows j*RPI + l/LPR, tokens X*(l%LPR)..+X) and
 // reads those tokens' probabilities from LDS.
 
@@ -432,10 +432,6 @@ struct ValuBody {
   static constexpr int RPI = 64 / LPR;             // value rows per load
   static constexpr int VJ = D / RPI;               // value loads per lane per tile
   static constexpr int TPB = BS / 16;              // tiles per block
-  // A 16-token tile of a 32-token block reads half of each value row; the
-  // other half belongs to the next tile, so those lines are loaded normally
-  // to let the second read hit.
-  static constexpr bool NTV = NT && TPB == 1;
   static_assert(KJ >= 1 && VJ >= 1, "unsupported shape");
 
   struct Tile {
@@ -486,14 +482,14 @@ struct ValuBody {
     const int blk = kt / TPB, sub = kt % TPB;
     const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
     // Tile `sub` of a block: keys start 16 tokens * X further into each
-    // [Bs][X] slab, values 16 tokens further into each [Bs] row.
+    // [Bs][X] slab; values are the sub-th [D][16] group.
     const KV *kb = reinterpret_cast<const KV *>(p.key_cache) + base + sub * 16 * X;
-    const KV *vb = reinterpret_cast<const KV *>(p.value_cache) + base + sub * 16;
+    const KV *vb = reinterpret_cast<const KV *>(p.value_cache) + base + sub * D * 16;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + t) * X);
 #pragma unroll
     for (int j = 0; j < VJ; ++j)
-      tl.v[j] = load_kv<u32x4, NTV>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X);
+      tl.v[j] = load_kv<u32x4, NT>(vb + (j * RPI + lane / LPR) * 16 + (lane % LPR) * X);
   }
 
   __device__ static void init(Acc &a) {
@@ -579,7 +575,7 @@ struct ValuBody {
     const int sub = (kt * 16) % BS / 16;
     const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
     KV *kb = reinterpret_cast<KV *>(p.key_cache) + base + sub * 16 * X;
-    KV *vb = reinterpret_cast<KV *>(p.value_cache) + base + sub * 16;
+    KV *vb = reinterpret_cast<KV *>(p.value_cache) + base + sub * D * 16;
     if ((t >> 2) == (r0 >> 2)) {
 #pragma unroll
       for (int j = 0; j < KJ; ++j)
@@ -587,7 +583,7 @@ struct ValuBody {
     }
 #pragma unroll
     for (int j = 0; j < VJ; ++j)
-      *reinterpret_cast<u32x4 *>(vb + (j * RPI + lane / LPR) * BS + (lane % LPR) * X) = tl.v[j];
+      *reinterpret_cast<u32x4 *>(vb + (j * RPI + lane / LPR) * 16 + (lane % LPR) * X) = tl.v[j];
   }
 
   // Combine the sum over the 16 token lanes and each row over its LPR lanes,
@@ -628,7 +624,7 @@ struct ValuBody {
 // same features).  The result gives lane l the logits of tokens 4g..4g+3
 // for head c.  P.V as O^T[d][h] = sum_t V^T[d][t] P^T[t][h] with
 // v_mfma_f32_16x16x16_bf16: A = 16 features x 16 tokens straight from the
-// [d][Bs] value rows (lane: feature c, tokens 4g..4g+3), B = the
+// [d][16] value rows (lane: feature c, tokens 4g..4g+3), B = the
 // probabilities exactly as the first product left them.  Every per-head
 // quantity (max, sum, rescale) therefore lives in lane%16 = head, and the
 // accumulators are rescaled by each lane's own factor.
@@ -639,8 +635,6 @@ struct MfmaBody {
   static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   static constexpr int VT = D / 16;   // 16-feature output tiles
   static constexpr int TPB = BS / 16;
-  // Value rows of a 32-token block are shared by two tiles: see ValuBody.
-  static constexpr bool NTV = NT && TPB == 1;
 
   struct Tile {
     u32x4 k[QJ];
@@ -699,11 +693,11 @@ struct MfmaBody {
     const int blk = kt / TPB, sub = kt % TPB;
     const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
     const bf16_t *kb = reinterpret_cast<const bf16_t *>(p.key_cache) + base + sub * 16 * 8;
-    const bf16_t *vb = reinterpret_cast<const bf16_t *>(p.value_cache) + base + sub * 16;
+    const bf16_t *vb = reinterpret_cast<const bf16_t *>(p.value_cache) + base + sub * D * 16;
 #pragma unroll
     for (int j = 0; j < QJ; ++j) tl.k[j] = load_kv<u32x4, NT>(kb + ((4 * j + g) * BS + c) * 8);
 #pragma unroll
-    for (int i = 0; i < VT; ++i) tl.v[i] = load_kv<u32x2, NTV>(vb + (16 * i + c) * BS + 4 * g);
+    for (int i = 0; i < VT; ++i) tl.v[i] = load_kv<u32x2, NT>(vb + (16 * i + c) * 16 + 4 * g);
   }
 
   __device__ static void init(Acc &a) {
@@ -792,7 +786,7 @@ struct MfmaBody {
     const int sub = (kt * 16) % BS / 16;
     const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
     bf16_t *kb = reinterpret_cast<bf16_t *>(p.key_cache) + base + sub * 16 * 8;
-    bf16_t *vb = reinterpret_cast<bf16_t *>(p.value_cache) + base + sub * 16;
+    bf16_t *vb = reinterpret_cast<bf16_t *>(p.value_cache) + base + sub * D * 16;
     if ((c >> 2) == (r0 >> 2)) {
 #pragma unroll
       for (int j = 0; j < QJ; ++j)
@@ -800,7 +794,7 @@ struct MfmaBody {
     }
 #pragma unroll
     for (int i = 0; i < VT; ++i)
-      *reinterpret_cast<u32x2 *>(vb + (16 * i + c) * BS + 4 * g) = tl.v[i];
+      *reinterpret_cast<u32x2 *>(vb + (16 * i + c) * 16 + 4 * g) = tl.v[i];
   }
 
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
@@ -1147,8 +1141,10 @@ hipError_t dispatch_out(const DecodeArgs &a, Params &p, bool use_mfma, hipStream
   }
   PA_CASE(64, 16)
   PA_CASE(64, 32)
+  PA_CASE(64, 64)
   PA_CASE(128, 16)
   PA_CASE(128, 32)
+  PA_CASE(128, 64)
 #undef PA_CASE
   return hipErrorInvalidValue;
 }

@@ -45,6 +45,7 @@ def _decode(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
     (dict(block_size=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=128), pa.PA_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), pa.PA_ERR_UNSUPPORTED),
     (dict(num_q_heads=6, num_kv_heads=4), pa.PA_ERR_INVALID_ARG),
     (dict(num_kv_heads=0), pa.PA_ERR_INVALID_ARG),

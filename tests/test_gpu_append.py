@@ -83,6 +83,8 @@ CASES = [
     ("7b", dict(batch=6, lens=(1, 16, 17, 33, 1100, 255))),                       # bf16 MHA
     ("70b", dict(batch=6, lens=(1, 16, 17, 32, 33, 700))),                        # G = 8
     ("70b", dict(batch=4, lens=(1, 31, 33, 400), block_size=32)),
+    ("70b", dict(batch=4, lens=(1, 63, 65, 400), block_size=64)),
+    ("7b", dict(batch=3, lens=(1, 64, 300), block_size=64)),
     ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=64, num_kv_heads=2)),    # G = 32
     ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=24, num_kv_heads=8,
                 head_dim=64)),                                                    # G = 3, d 64

@@ -37,6 +37,8 @@ SMALL = [
     ("7b", dict(batch=5, lens=(1, 16, 17, 1100, 255))),            # >64 blocks: 2 table chunks
     ("70b", dict(batch=6, len_range=(1, 700))),
     ("70b", dict(batch=3, len_range=(100, 400), block_size=32)),
+    ("70b", dict(batch=4, lens=(1, 63, 65, 400), block_size=64)),
+    ("7b", dict(batch=3, lens=(64, 129, 300), block_size=64)),                   # VALU, Bs 64
     ("long", dict(batch=2, lens=(3000, 1500))),
     ("long", dict(batch=2, lens=(3000, 1501), block_size=32)),
     ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=8, num_kv_heads=4)),    # G = 2
@@ -77,7 +79,8 @@ def test_fp32_and_bf16_outputs(gpu, name, kw):
 # sampled sequences the oracle computes one by one.
 FULL = [("7b", {}, 512), ("70b", {}, 512), ("long", {}, 512), ("long", dict(block_size=32), 512),
         ("7b", {}, 0), ("7b", {}, BAL), ("70b", {}, BAL), ("long", {}, BAL),
-        ("long", dict(block_size=32), BAL)]
+        ("long", dict(block_size=32), BAL), ("long", dict(block_size=64), BAL),
+        ("70b", dict(block_size=64), BAL)]
 
 
 @pytest.mark.parametrize("name,kw,ps", FULL)
@@ -162,8 +165,9 @@ def _host_pools(case):
     x = 16 // np.dtype(dt).itemsize
     kp = W.host_array(case.key_cache).reshape(case.num_blocks, case.num_kv_heads,
                                               case.head_dim // x, case.block_size, x)
+    t = pl.value_group(case.block_size)
     vp = W.host_array(case.value_cache).reshape(case.num_blocks, case.num_kv_heads,
-                                                case.head_dim, case.block_size)
+                                                case.block_size // t, case.head_dim, t)
     return kp, vp, dt
 
 

@@ -106,7 +106,7 @@ def test_bf16_bits_survive_the_scatter_unchanged():
     oracle.reshape_and_cache(key, key, kp, vp, np.array([3], np.int64), num_kv_heads=1,
                              head_dim=8, block_size=16, num_blocks=1)
     assert np.array_equal(kp[0, 0, 0, 3], key[0, 0])
-    assert np.array_equal(vp[0, 0, :, 3], key[0, 0])
+    assert np.array_equal(vp[0, 0, 0, :, 3], key[0, 0])
 
 
 # ---- swap_blocks (inferensys glossary, third and fifth paragraphs) -----------

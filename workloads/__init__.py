@@ -247,13 +247,14 @@ class SharedPrefixPlan:
 
 
 def shared_plan(*, batch: Optional[int] = None, prompt: Optional[int] = None,
-                tail_range=None, seed: Optional[int] = None) -> SharedPrefixPlan:
+                tail_range=None, seed: Optional[int] = None,
+                block_size: Optional[int] = None) -> SharedPrefixPlan:
     cfg = CONFIGS["shared"]
     seed = seed_for("shared") if seed is None else seed
     b = batch or cfg["batch"]
     p = cfg["prompt"] if prompt is None else prompt
     lo, hi = tail_range or cfg["tail_range"]
-    bs = cfg["block_size"]
+    bs = block_size or cfg["block_size"]
     rng = np.random.default_rng(seed)
     tails = rng.integers(lo, hi + 1, size=b).astype(np.int64)
     # Blocks alive at the peak of a step: the shared prompt, every private
