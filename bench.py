@@ -333,6 +333,8 @@ def main():
                     help="block size of the workload (default: the workload's own)")
     ap.add_argument("--table-order", choices=["random", "identity"], default="random",
                     help="physical blocks in random order (paged) or consecutive (contiguous)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph")
     ap.add_argument("--waste-report", action="store_true",
                     help="only print the allocator's KV waste per workload and block size "
                          "(host only)")
@@ -453,6 +455,26 @@ def main():
         "wall_s_timed_loop": round(wall, 4),
         "roofline": roof,
     }
+    if args.graph:
+        step.capture()
+        g_s, g_e = [ev() for _ in range(K)], [ev() for _ in range(K)]
+        torch.cuda.synchronize()
+        for _ in range(W_):
+            if flush is not None:
+                flush.sum()
+            step.replay()
+        for i in range(K):
+            if flush is not None:
+                flush.sum()
+            g_s[i].record()
+            step.replay()
+            g_e[i].record()
+        torch.cuda.synchronize()
+        g_ms = [a.elapsed_time(b) for a, b in zip(g_s, g_e)]
+        result["graph"] = {"ms_per_step": round(float(np.mean(g_ms)), 4),
+                           "step_ms_median": round(float(np.median(g_ms)), 4),
+                           "value_GBs": round(kv_bytes / (float(np.mean(g_ms)) / 1e3) / 1e9, 1)}
+        log("graph replay: step %.1f us" % (float(np.mean(g_ms)) * 1e3))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(step, lens, args.cpu_seconds)

@@ -198,6 +198,7 @@ size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 a negative slot skips the token.  Slots must be
  *                 < num_blocks * block_size and distinct (a repeated slot is
  *                 a caller error; PA_VALIDATE=1 rejects it).
+ *  block_size must be a multiple of 16 (PA_ERR_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
 pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
                                void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
@@ -218,6 +219,27 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
 pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int64_t *block_mapping,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int64_t num_blocks, pa_dtype dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Every layer at once.  A model keeps one pair of pools per layer and
+ * writes one new token per sequence into each of them per decode step; the
+ * copy of copy-on-write applies to every layer too.  These calls do that in
+ * one launch instead of one per layer.  key_caches, value_caches (and keys,
+ * values) are device arrays of num_layers pointers, one per layer, each as
+ * in the single-layer call (PA_VALIDATE=1 checks every pointer); all
+ * layers share the shapes, the slots and the block mapping.
+ * ---------------------------------------------------------------------- */
+pa_status pa_reshape_and_cache_layers(const void *const *keys, const void *const *values,
+                                      void *const *key_caches, void *const *value_caches,
+                                      int32_t num_layers, const int64_t *slot_mapping,
+                                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                      void *stream);
+pa_status pa_copy_blocks_layers(void *const *key_caches, void *const *value_caches,
+                                int32_t num_layers, const int64_t *block_mapping,
+                                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                void *stream);
 
 /* ------------------------------------------------------------------------
  * swap_blocks -- the copy half of swapping a preempted sequence's blocks to

@@ -8,6 +8,8 @@ Python binding:
     per-sequence block tables (HIP kernels; MFMA for grouped-query heads);
   * ``reshape_and_cache`` -- write new tokens' K/V into their slots;
   * ``copy_blocks`` -- the copy of copy-on-write;
+  * ``reshape_and_cache_layers``, ``copy_blocks_layers`` -- both over every
+    layer's pools in one launch;
   * ``swap_blocks`` -- block copies between GPU and pinned host pools;
   * ``BlockAllocator`` -- host free list, refcounts, copy-on-write and a
     swap space for preempted sequences.
@@ -18,4 +20,4 @@ from ._binding import (  # noqa: F401
     PA_PARTITION_BALANCED, BlockAllocator, PagedAttnError,
     allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
     paged_attention_workspace_bytes, reshape_and_cache, set_balance_weights, set_timing_events,
-    swap_blocks, value_cache_shape)
+    swap_blocks, value_cache_shape, pointer_array, reshape_and_cache_layers, copy_blocks_layers)

@@ -36,6 +36,7 @@ EXPORTS = (
     "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
     "pa_set_balance_weights",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks",
+    "pa_reshape_and_cache_layers", "pa_copy_blocks_layers",
     "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free",
     "pa_allocator_block_size", "pa_seq_create", "pa_seq_fork", "pa_seq_append_slot",
     "pa_seq_free", "pa_seq_block_table", "pa_seq_len", "pa_block_refcount",
@@ -72,6 +73,9 @@ def _declare(lib):
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32, vp]),
+        "pa_reshape_and_cache_layers": (i32, [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i64,
+                                              i32, vp]),
+        "pa_copy_blocks_layers": (i32, [vp, vp, i32, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_allocator_set_swap_space": (i32, [vp, i64]),
         "pa_allocator_num_free_host": (i64, [vp]),
         "pa_host_block_refcount": (i32, [vp, i32]),
@@ -147,13 +151,17 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code_of(dtype) -> int:
     torch = _torch()
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return PA_FP32
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return PA_BF16
-    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dtype)
+
+
+def _dtype_code(t) -> int:
+    return _dtype_code_of(t.dtype)
 
 
 def _dev(t, name, device=None):
@@ -365,6 +373,55 @@ def swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, 
         src_value_cache.data_ptr(), block_mapping.data_ptr(), block_mapping.numel() // 2,
         num_kv_heads, head_dim, block_size, int(src_key_cache.shape[0]),
         int(dst_key_cache.shape[0]), _dtype_code(src_key_cache), _stream(dev, stream)))
+
+
+def pointer_array(tensors, device):
+    """int64 device tensor of the tensors' data pointers (for the per-layer calls).
+    Build it once per set of pools: it is an upload."""
+    torch = _torch()
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    for t in tensors:
+        _dev(t, "per-layer tensor", device)
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def reshape_and_cache_layers(key_ptrs, value_ptrs, key_cache_ptrs, value_cache_ptrs,
+                             slot_mapping, *, num_layers: int, num_kv_heads: int, head_dim: int,
+                             block_size: int, num_blocks: int, dtype, stream=None):
+    """reshape_and_cache on every layer in one launch; the *_ptrs are
+    pointer_array() tensors of the per-layer keys, values and pools."""
+    lib = load()
+    dev = slot_mapping.device
+    for t, n in ((key_ptrs, "key_ptrs"), (value_ptrs, "value_ptrs"),
+                 (key_cache_ptrs, "key_cache_ptrs"), (value_cache_ptrs, "value_cache_ptrs")):
+        _dev(t, n, dev)
+        if t.dtype != _torch().int64 or t.numel() != num_layers:
+            raise ValueError("%s must be int64 [num_layers]" % n)
+    _check(lib.pa_reshape_and_cache_layers(
+        key_ptrs.data_ptr(), value_ptrs.data_ptr(), key_cache_ptrs.data_ptr(),
+        value_cache_ptrs.data_ptr(), int(num_layers), slot_mapping.data_ptr(),
+        int(slot_mapping.numel()), num_kv_heads, head_dim, block_size, int(num_blocks),
+        _dtype_code_of(dtype), _stream(dev, stream)))
+
+
+def copy_blocks_layers(key_cache_ptrs, value_cache_ptrs, block_mapping, *, num_layers: int,
+                       num_kv_heads: int, head_dim: int, block_size: int, num_blocks: int, dtype,
+                       stream=None):
+    """copy_blocks on every layer in one launch (pointer_array() pools)."""
+    lib = load()
+    dev = block_mapping.device
+    for t, n in ((key_cache_ptrs, "key_cache_ptrs"), (value_cache_ptrs, "value_cache_ptrs")):
+        _dev(t, n, dev)
+        if t.dtype != _torch().int64 or t.numel() != num_layers:
+            raise ValueError("%s must be int64 [num_layers]" % n)
+    if block_mapping.dtype != _torch().int64 or block_mapping.numel() % 2:
+        raise ValueError("block_mapping must be int64 [num_pairs, 2]")
+    _check(lib.pa_copy_blocks_layers(
+        key_cache_ptrs.data_ptr(), value_cache_ptrs.data_ptr(), int(num_layers),
+        block_mapping.data_ptr(), block_mapping.numel() // 2, num_kv_heads, head_dim,
+        block_size, int(num_blocks), _dtype_code_of(dtype), _stream(dev, stream)))
 
 
 # ---- allocator -----------------------------------------------------------------

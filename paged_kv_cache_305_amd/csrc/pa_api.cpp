@@ -350,6 +350,9 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
   if ((head_dim * esz) % 16 != 0)
     return pa_fail(PA_ERR_UNSUPPORTED, "%s: head_dim * element size must be a multiple of 16",
                    fn);
+  if (block_size % 16 != 0)   // values are stored in 16-token groups
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block_size %d is not a multiple of 16", fn,
+                   block_size);
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -372,6 +375,121 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
   const int e = pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
                                              num_tokens, num_kv_heads, head_dim, block_size,
                                              num_blocks, esz, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+namespace {
+
+// PA_VALIDATE: every per-layer pointer must be 16-byte aligned device memory.
+pa_status check_layer_pointers(const char *fn, const void *const *arr, int32_t n,
+                               const char *what, void *stream) {
+  std::vector<uintptr_t> host;
+  pa_status s = to_host(host, reinterpret_cast<const uintptr_t *>(arr), (size_t)n, stream);
+  if (s != PA_OK) return s;
+  for (int32_t l = 0; l < n; ++l) {
+    const void *p = reinterpret_cast<const void *>(host[(size_t)l]);
+    if (!p || !aligned16(p) || !device_addressable(p))
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: %s[%d] is not 16-byte aligned device memory", fn,
+                     what, l);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_reshape_and_cache_layers(const void *const *keys, const void *const *values,
+                                      void *const *key_caches, void *const *value_caches,
+                                      int32_t num_layers, const int64_t *slot_mapping,
+                                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                      void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_reshape_and_cache_layers";
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_FP32 or PA_BF16", fn);
+  if (num_layers < 0 || num_layers > 65535 || num_tokens < 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: bad sizes (num_layers in [0, 65535])", fn);
+  if ((head_dim * esz) % 16 != 0 || block_size % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: head_dim * element size and block_size must be "
+                   "multiples of 16", fn);
+  if (num_tokens == 0 || num_layers == 0) return PA_OK;
+  if (!keys || !values || !key_caches || !value_caches || !slot_mapping)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (deep_validation()) {
+    pa_status s = check_layer_pointers(fn, keys, num_layers, "keys", stream);
+    if (s == PA_OK) s = check_layer_pointers(fn, values, num_layers, "values", stream);
+    if (s == PA_OK)
+      s = check_layer_pointers(fn, (const void *const *)key_caches, num_layers, "key_caches",
+                               stream);
+    if (s == PA_OK)
+      s = check_layer_pointers(fn, (const void *const *)value_caches, num_layers,
+                               "value_caches", stream);
+    if (s != PA_OK) return s;
+    std::vector<int64_t> slots;
+    s = to_host(slots, slot_mapping, (size_t)num_tokens, stream);
+    if (s != PA_OK) return s;
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (slots[i] < 0) continue;
+      if (slots[i] >= num_blocks * block_size || !seen.insert(slots[i]).second)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: slot_mapping[%d] = %lld out of range or "
+                       "repeated", fn, i, (long long)slots[i]);
+    }
+  }
+  const int e = pa::launch_reshape_and_cache_layers(keys, values, key_caches, value_caches,
+                                                    num_layers, slot_mapping, num_tokens,
+                                                    num_kv_heads, head_dim, block_size,
+                                                    num_blocks, esz, stream);
+  return e == 0 ? PA_OK : hip_fail(fn, e);
+}
+
+pa_status pa_copy_blocks_layers(void *const *key_caches, void *const *value_caches,
+                                int32_t num_layers, const int64_t *block_mapping,
+                                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                                void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_copy_blocks_layers";
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return pa_fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_FP32 or PA_BF16", fn);
+  if (num_layers < 0 || num_layers > 32767 || num_pairs < 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: bad sizes (num_layers in [0, 32767])", fn);
+  const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * esz;
+  if (block_bytes % 16 != 0)
+    return pa_fail(PA_ERR_UNSUPPORTED, "%s: block bytes must be a multiple of 16", fn);
+  if (num_pairs == 0 || num_layers == 0) return PA_OK;
+  if (!key_caches || !value_caches || !block_mapping)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (deep_validation()) {
+    pa_status s = check_layer_pointers(fn, (const void *const *)key_caches, num_layers,
+                                       "key_caches", stream);
+    if (s == PA_OK)
+      s = check_layer_pointers(fn, (const void *const *)value_caches, num_layers,
+                               "value_caches", stream);
+    if (s != PA_OK) return s;
+    std::vector<int64_t> m;
+    s = to_host(m, block_mapping, (size_t)num_pairs * 2, stream);
+    if (s != PA_OK) return s;
+    std::unordered_set<int64_t> srcs, dsts;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      for (int k = 0; k < 2; ++k)
+        if (m[2 * i + k] < 0 || m[2 * i + k] >= num_blocks)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: block_mapping[%d][%d] out of range", fn, i, k);
+      srcs.insert(m[2 * i]);
+      if (!dsts.insert(m[2 * i + 1]).second)
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: destination %lld repeats", fn,
+                       (long long)m[2 * i + 1]);
+    }
+    for (int64_t d : dsts)
+      if (srcs.count(d))
+        return pa_fail(PA_ERR_INVALID_ARG, "%s: block %lld is both a source and a destination",
+                       fn, (long long)d);
+  }
+  const int e = pa::launch_copy_blocks_layers(key_caches, value_caches, num_layers,
+                                              block_mapping, num_pairs, block_bytes, num_blocks,
+                                              stream);
   return e == 0 ? PA_OK : hip_fail(fn, e);
 }
 

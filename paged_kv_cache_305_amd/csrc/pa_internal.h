@@ -70,6 +70,14 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
                              void *value_cache, const int64_t *slots, int32_t num_tokens,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int64_t num_blocks, int32_t elem_bytes, void *stream);
+int launch_reshape_and_cache_layers(const void *const *keys, const void *const *values,
+                                    void *const *key_caches, void *const *value_caches,
+                                    int32_t num_layers, const int64_t *slots, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int64_t num_blocks, int32_t elem_bytes, void *stream);
+int launch_copy_blocks_layers(void *const *key_caches, void *const *value_caches,
+                              int32_t num_layers, const int64_t *pairs, int32_t num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, void *stream);
 int launch_copy_blocks(void *dst_key, void *dst_value, const void *src_key,
                        const void *src_value, const int64_t *pairs, int32_t num_pairs,
                        int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks, void *stream);

@@ -88,6 +88,27 @@ class DecodeStep:
             return self.fused
         return int(self.query.shape[0]) * self.num_kv_heads <= self.FUSED_MAX_ROWS
 
+    def capture(self):
+        """Record run() into a HIP graph (torch.cuda.CUDAGraph); replay()
+        then repeats the step's launches with one call.  The graph reads
+        and writes the step's tensors in place: refill them (copy_) to run
+        the step on new inputs."""
+        import torch
+        side = torch.cuda.Stream()             # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()                         # settle lazy set-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        self._graph = g
+        return g
+
+    def replay(self):
+        self._graph.replay()
+        return self.out
+
     def run(self, stream=None):
         """copy_blocks, then either one launch that writes the new tokens and
         attends (fused) or reshape_and_cache followed by attention."""

@@ -115,6 +115,9 @@ def test_cache_calls_reject_bad_arguments():
                                     pa.PA_BF16, NULL) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_reshape_and_cache(NULL, NULL, NULL, NULL, NULL, 0, 8, 128, 16, 10,
                                     pa.PA_BF16, NULL) == pa.PA_OK
+    # Values are stored in 16-token groups: other block sizes are refused.
+    assert lib.pa_reshape_and_cache(NULL, NULL, NULL, NULL, NULL, 1, 8, 128, 8, 10,
+                                    pa.PA_BF16, NULL) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_copy_blocks(NULL, NULL, NULL, 0, 8, 128, 16, 10, pa.PA_BF16, NULL) == pa.PA_OK
     assert lib.pa_copy_blocks(NULL, NULL, NULL, 3, 8, 128, 16, 10, pa.PA_BF16, NULL) == \
         pa.PA_ERR_INVALID_ARG
