@@ -56,7 +56,7 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def build_step(name, ps, device, block_size=None, table_order="random"):
+def build_step(name, ps, device, block_size=None, table_order="random", prefix=True):
     import workloads as W
     from paged_kv_cache_305_amd.step import shared_prefix_step, step_from_case
     if name == "shared":
@@ -64,7 +64,7 @@ def build_step(name, ps, device, block_size=None, table_order="random"):
             raise SystemExit("the shared-prefix tables come from the allocator")
         plan = W.shared_plan(block_size=block_size)
         tens = W.shared_tensors(plan, device=device)
-        step, rec = shared_prefix_step(plan, tens, partition_size=ps)
+        step, rec = shared_prefix_step(plan, tens, partition_size=ps, prefix=prefix)
         lens = rec["lens"].astype(np.int64)
         return step, lens, dict(seed=plan.seed, cow_pairs=int(rec["pairs"].shape[0]),
                                 num_blocks=plan.num_blocks, block_size=plan.block_size)
@@ -333,6 +333,9 @@ def main():
                     help="block size of the workload (default: the workload's own)")
     ap.add_argument("--table-order", choices=["random", "identity"], default="random",
                     help="physical blocks in random order (paged) or consecutive (contiguous)")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="shared workload: attend each sequence over its whole table instead "
+                         "of reading the shared prompt once for all")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph")
     ap.add_argument("--waste-report", action="store_true",
@@ -369,7 +372,8 @@ def main():
 
     log("building workload %s" % args.workload)
     step, lens, info = build_step(args.workload, args.partition_size, device,
-                                  block_size=args.block_size, table_order=args.table_order)
+                                  block_size=args.block_size, table_order=args.table_order,
+                                  prefix=not args.no_prefix)
     step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
@@ -417,6 +421,8 @@ def main():
     body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
                           step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
     kernel = "%s<%s>" % ("decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
+    if step.prefix_len:
+        kernel = "decode_prefix + " + kernel
     roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=counter_traffic(args.workload, args.partition_size),
@@ -438,6 +444,7 @@ def main():
         "config": {"workload": WORKLOADS[args.workload], "partition_size": args.partition_size,
                    "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
                    "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
+                   "shared_prefix_tokens": step.prefix_len,
                    "cache_write": "inside the attention launch" if step.uses_fused_write
                                   else "reshape_and_cache before the attention",
                    "flush_between_steps": flush is not None, **info,

@@ -160,6 +160,38 @@ pa_status pa_paged_attention_decode_append(
     int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
     pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * paged_attention_decode_prefix -- the same attention when every sequence
+ * starts with the same prefix_len tokens stored in the same physical blocks
+ * (parallel samples or beam candidates of one prompt: inferensys glossary
+ * "Paged Attention", second paragraph; the skillsintelligence glossary's
+ * worked example of a 4,000-token prompt stored once for ten users).  The
+ * prefix blocks are read once per KV head for all num_seqs * G query rows
+ * (MFMA tiles), each sequence's own tokens after the prefix as in
+ * pa_paged_attention_decode, and the two combined exactly by log-sum-exp.
+ *
+ *  prefix_len     positive multiple of block_size, <= every context_lens[i];
+ *                 block_tables rows agree on their first prefix_len /
+ *                 block_size entries (PA_VALIDATE=1 checks both).
+ *  workspace      pa_paged_attention_prefix_workspace_bytes(...) bytes.
+ *  Needs bf16 K/V (PA_ERR_UNSUPPORTED otherwise); other arguments as in
+ *  pa_paged_attention_decode, with the balanced split.
+ * ---------------------------------------------------------------------- */
+pa_status pa_paged_attention_decode_prefix(void *out, const void *query, const void *key_cache,
+                                           const void *value_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, float scale,
+                                           int32_t prefix_len, pa_dtype kv_dtype,
+                                           pa_dtype out_dtype, uint32_t flags, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim,
+                                                 int32_t max_context_len, int32_t prefix_len,
+                                                 pa_dtype kv_dtype);
+
 /* Tracing hook: while set, every pa_paged_attention_decode(_append) call
  * records hipEvent_t `before_main` just before its main attention kernel and
  * `after_main` just after it, on the call's stream (the log-sum-exp merge

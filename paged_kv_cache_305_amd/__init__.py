@@ -6,6 +6,8 @@ Python binding:
 
   * ``paged_attention_decode`` -- single-query attention read through
     per-sequence block tables (HIP kernels; MFMA for grouped-query heads);
+  * ``paged_attention_decode_prefix`` -- the same with a prefix shared by
+    every sequence read once for all of them;
   * ``reshape_and_cache`` -- write new tokens' K/V into their slots;
   * ``copy_blocks`` -- the copy of copy-on-write;
   * ``reshape_and_cache_layers``, ``copy_blocks_layers`` -- both over every
@@ -20,4 +22,5 @@ from ._binding import (  # noqa: F401
     PA_PARTITION_BALANCED, BlockAllocator, PagedAttnError,
     allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
     paged_attention_workspace_bytes, reshape_and_cache, set_balance_weights, set_timing_events,
-    swap_blocks, value_cache_shape, pointer_array, reshape_and_cache_layers, copy_blocks_layers)
+    swap_blocks, value_cache_shape, pointer_array, reshape_and_cache_layers, copy_blocks_layers,
+    paged_attention_decode_prefix, paged_attention_prefix_workspace_bytes)

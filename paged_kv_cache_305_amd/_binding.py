@@ -33,6 +33,7 @@ PA_DECODE_KV_REUSED = 1
 EXPORTS = (
     "pa_last_error", "pa_version",
     "pa_paged_attention_decode", "pa_paged_attention_decode_append",
+    "pa_paged_attention_decode_prefix", "pa_paged_attention_prefix_workspace_bytes",
     "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
     "pa_set_balance_weights",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks",
@@ -68,6 +69,10 @@ def _declare(lib):
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                   i32, i32, i64, i32, f32, i32, i32, i32,
+                                                   ctypes.c_uint32, vp, sz, vp]),
+        "pa_paged_attention_prefix_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_set_timing_events": (i32, [vp, vp]),
         "pa_set_balance_weights": (i32, [vp, i32]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
@@ -231,6 +236,47 @@ def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_di
     return int(load().pa_paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                          head_dim, max_context_len,
                                                          partition_size, code))
+
+
+def paged_attention_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_context_len, prefix_len, kv_dtype) -> int:
+    lib = load()
+    return int(lib.pa_paged_attention_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, prefix_len,
+        _dtype_code_of(kv_dtype)))
+
+
+def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tables,
+                                  context_lens, *, prefix_len: int, num_kv_heads: int,
+                                  block_size: int, max_context_len: int, scale: float,
+                                  workspace=None, num_blocks: Optional[int] = None,
+                                  stream=None):
+    """Decode attention when every sequence's first prefix_len tokens are the
+    same physical blocks (sequence 0's): those are read once for all rows."""
+    lib = load()
+    dev = query.device
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _dev(t, n, dev)
+    torch = _torch()
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    B, hq, d = query.shape
+    if tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must have the query's shape")
+    nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    need = paged_attention_prefix_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
+                                                  prefix_len, query.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.pa_paged_attention_decode_prefix(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
+        int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(prefix_len),
+        _dtype_code(query), _dtype_code(out), 0, _dev(workspace, "workspace", dev).data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(dev, stream)))
+    return out
 
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, *,

@@ -100,15 +100,36 @@ void balance_weights(int32_t out[8]) {
   for (int i = 0; i < 8; ++i) out[i] = g_xcd_weights[i].load(std::memory_order_relaxed);
 }
 
-WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments) {
-  WorkspaceLayout w{rows, 0, 0, 0, 0, 0};
-  if (rows == 0) return w;
+WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments,
+                                 size_t prefix_rows) {
+  WorkspaceLayout w{rows, 0, 0, 0, 0, 0, 0, 0, 0};
+  if (rows == 0 && prefix_rows == 0) return w;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.sum_off = up(rows * sizeof(float));
   w.acc_off = w.sum_off + up(rows * sizeof(float));
   w.seg_off = w.acc_off + up(rows * (size_t)head_dim * sizeof(float));
-  w.total = w.seg_off + up(segments * 2 * sizeof(int32_t));
+  w.pf_max_off = w.seg_off + up(segments * 2 * sizeof(int32_t));
+  w.pf_sum_off = w.pf_max_off + up(prefix_rows * sizeof(float));
+  w.pf_acc_off = w.pf_sum_off + up(prefix_rows * sizeof(float));
+  w.total = w.pf_acc_off + up(prefix_rows * (size_t)head_dim * sizeof(float));
   return w;
+}
+
+PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t prefix_len, int cus) {
+  PrefixPlan pl{0, 0, 0, 0, 0};
+  if (prefix_len <= 0 || num_seqs <= 0 || num_kv_heads <= 0) return pl;
+  const int tiles = prefix_len / 16;
+  pl.rows = num_seqs * (num_q_heads / num_kv_heads);
+  pl.row_blocks = (pl.rows + 16 * kPrefixRowTiles - 1) / (16 * kPrefixRowTiles);
+  const int64_t per_chunk = (int64_t)pl.row_blocks * num_kv_heads;
+  int64_t chunks = ((int64_t)cus * kPrefixWavesPerCU + per_chunk - 1) / per_chunk;
+  if (chunks < 1) chunks = 1;
+  if (chunks > tiles) chunks = tiles;
+  pl.chunk_tiles = (int)((tiles + chunks - 1) / chunks);
+  pl.chunks = (tiles + pl.chunk_tiles - 1) / pl.chunk_tiles;
+  pl.partial_rows = (size_t)pl.chunks * num_kv_heads * pl.rows;
+  return pl;
 }
 
 }  // namespace pa
@@ -170,7 +191,8 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                       float scale, int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
-                      uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+                      uint32_t flags, void *workspace, size_t workspace_bytes, void *stream,
+                      int32_t prefix_len = 0) {
   const bool appending = new_key != nullptr || new_value != nullptr || slot_mapping != nullptr;
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -197,6 +219,14 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                    "multiple of block_size %d", fn, partition_size, block_size);
   if ((flags & ~PA_DECODE_KV_REUSED) != 0)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+  if (prefix_len != 0) {
+    if (kv_dtype != PA_BF16)
+      return pa_fail(PA_ERR_UNSUPPORTED, "%s: a shared prefix needs bf16 K/V (MFMA)", fn);
+    if (prefix_len < 0 || prefix_len % block_size != 0 || prefix_len > max_context_len)
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: prefix_len %d must be a positive multiple of "
+                     "block_size %d and <= max_context_len %d", fn, prefix_len, block_size,
+                     max_context_len);
+  }
   if (num_seqs == 0) return PA_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -215,9 +245,11 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
   const int32_t bound = partition_size < 0 ? balanced_wave_bound() : 0;
   if (partition_size < 0 && bound == 0)
     return pa_fail(PA_ERR_HIP, "%s: cannot query the current device", fn);
+  const pa::PrefixPlan pf = pa::prefix_plan(num_seqs, num_q_heads, num_kv_heads, prefix_len,
+                                            bound / 32);
   const pa::WorkspaceLayout ws = pa::workspace_layout(
       partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
-      partition_size < 0 ? (size_t)num_seqs * hu.units : 0);
+      partition_size < 0 ? (size_t)num_seqs * hu.units : 0, pf.partial_rows);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu", fn,
@@ -242,6 +274,18 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
         if (b < 0 || b >= num_blocks)
           return pa_fail(PA_ERR_INVALID_ARG, "%s: block_tables[%d][%d] = %d outside [0, %lld)",
                          fn, i, j, b, (long long)num_blocks);
+      }
+    }
+    if (prefix_len > 0) {
+      // Every sequence holds the prefix, in the same blocks as sequence 0.
+      for (int32_t i = 0; i < num_seqs; ++i) {
+        if (lens[i] < prefix_len)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: context_lens[%d] = %d < prefix_len %d", fn, i,
+                         lens[i], prefix_len);
+        for (int32_t j = 0; j < prefix_len / block_size; ++j)
+          if (tabs[(size_t)i * max_blocks_per_seq + j] != tabs[(size_t)j])
+            return pa_fail(PA_ERR_INVALID_ARG, "%s: block_tables[%d][%d] differs from sequence "
+                           "0's prefix block", fn, i, j);
       }
     }
     if (appending) {
@@ -294,6 +338,10 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
   a.ws_sum = ws.total ? reinterpret_cast<float *>(wsb + ws.sum_off) : nullptr;
   a.ws_acc = ws.total ? reinterpret_cast<float *>(wsb + ws.acc_off) : nullptr;
   a.seg_units = ws.total ? reinterpret_cast<int32_t *>(wsb + ws.seg_off) : nullptr;
+  a.prefix_len = prefix_len;
+  a.pf_max = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_max_off) : nullptr;
+  a.pf_sum = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_sum_off) : nullptr;
+  a.pf_acc = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_acc_off) : nullptr;
   pa::balance_weights(a.xcd_weights);
   a.ev_before_main = g_ev_before_main;
   a.ev_after_main = g_ev_after_main;
@@ -320,6 +368,45 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
                      max_context_len, scale, partition_size, kv_dtype, out_dtype, flags,
                      workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_prefix(void *out, const void *query, const void *key_cache,
+                                           const void *value_cache, const int32_t *block_tables,
+                                           const int32_t *context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                                           int32_t max_context_len, float scale,
+                                           int32_t prefix_len, pa_dtype kv_dtype,
+                                           pa_dtype out_dtype, uint32_t flags, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+  pa_clear_error();
+  const char *fn = "pa_paged_attention_decode_prefix";
+  if (prefix_len <= 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: prefix_len must be positive", fn);
+  return decode_call(fn, out, query, key_cache, value_cache, nullptr, nullptr, nullptr,
+                     block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                     PA_PARTITION_BALANCED, kv_dtype, out_dtype, flags, workspace,
+                     workspace_bytes, stream, prefix_len);
+}
+
+size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim,
+                                                 int32_t max_context_len, int32_t prefix_len,
+                                                 pa_dtype kv_dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_context_len < 0 ||
+      prefix_len <= 0 || kv_dtype != PA_BF16)
+    return 0;
+  const pa::HeadUnits hu = pa::head_units(num_q_heads, num_kv_heads, kv_dtype);
+  const int32_t bound = balanced_wave_bound();
+  if (bound == 0) return 0;
+  const pa::PrefixPlan pf = pa::prefix_plan(num_seqs, num_q_heads, num_kv_heads, prefix_len,
+                                            bound / 32);
+  return pa::workspace_layout(partial_rows(num_seqs, hu, max_context_len, -1, bound), head_dim,
+                              (size_t)num_seqs * hu.units, pf.partial_rows)
+      .total;
 }
 
 pa_status pa_paged_attention_decode_append(

@@ -229,6 +229,14 @@ struct Params {
   int64_t id_stride;    // balanced mode: piece ids per sub-problem
   int xcd_prefix[9];    // balanced mode: prefix sums of the 8 per-XCD weights
   float scale_log2e;
+  // Shared prefix (0 tiles when unused): every sequence's first
+  // prefix_tiles * 16 tokens are the same physical blocks, those of
+  // sequence 0.  decode_prefix covers them for all query rows at once and
+  // the balanced split only the tiles after them.
+  int prefix_tiles;
+  int pf_chunks, pf_chunk_tiles;   // prefix split into chunks of tiles
+  int pf_rows;                     // query rows per KV head: num_seqs * group
+  float *pf_max, *pf_sum, *pf_acc; // partials [chunk][KV head][row]
 };
 
 __device__ __forceinline__ int seq_len(const Params &p, int i) {
@@ -237,6 +245,13 @@ __device__ __forceinline__ int seq_len(const Params &p, int i) {
 }
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + 15) >> 4; }
+
+// Tiles of a sequence the per-sequence pieces cover: those after the
+// shared prefix.
+__device__ __forceinline__ int own_tiles(const Params &p, int L) {
+  const int n = tiles_of(L) - p.prefix_tiles;
+  return n > 0 ? n : 0;
+}
 
 // One contiguous tile range [t0/16, ceil(t1/16)) of segment (seq, unit).
 struct Piece {
@@ -897,7 +912,7 @@ __device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
   int64_t tot = 0;
   for (int c = 0; c < p.num_seqs; c += 64) {
     const int i = c + ((int)threadIdx.x & 63);
-    tot += wave_sum(i < p.num_seqs ? tiles_of(seq_len(p, i)) : 0);
+    tot += wave_sum(i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0);
   }
   return tot;
 }
@@ -957,8 +972,9 @@ struct RangePieces {
       if (a == 0) p->seg_units[2 * g] = (int32_t)unit;
       if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
     }
-    out = Piece{seq, u, a * 16, min(b * 16, L), a == 0 && b == n_seq, b == n_seq,
-                id_base + (int64_t)seq * ux + k + unit, -1};
+    const int pt = p->prefix_tiles;
+    out = Piece{seq, u, (a + pt) * 16, min((b + pt) * 16, L), pt == 0 && a == 0 && b == n_seq,
+                b == n_seq, id_base + (int64_t)seq * ux + k + unit, -1};
     t += len;
     a = 0;
     if (t < te && ++k == ux) {
@@ -969,7 +985,7 @@ struct RangePieces {
           break;
         }
         L = lens.get(*p, seq);
-        n_seq = tiles_of(L);
+        n_seq = own_tiles(*p, L);
       } while (n_seq == 0);
     }
     return true;
@@ -995,7 +1011,7 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   int64_t seq_first = 0, base = 0;
   for (int c = 0; c < p.num_seqs && gen.seq < 0; c += 64) {
     const int i = c + lane;
-    const int n = i < p.num_seqs ? tiles_of(seq_len(p, i)) : 0;
+    const int n = i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0;
     const int incl = wave_incl_scan(n);
     const uint64_t hit = __builtin_amdgcn_ballot_w64((base + incl) * gen.ux > gen.t);
     if (hit) {
@@ -1012,6 +1028,129 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   gen.k = (int)((gen.t - seq_first) / gen.n_seq);
   gen.a = (int)((gen.t - seq_first) % gen.n_seq);
   stream_pieces<Body>(p, gen, p_lds);
+}
+
+// ---- shared prefix -------------------------------------------------------------
+//
+// When every sequence starts with the same physical blocks (a prompt shared
+// by parallel samples: inferensys glossary "Paged Attention", second
+// paragraph; skillsintelligence glossary, worked example), those blocks are
+// read once per KV head for all the query rows that use them: the rows
+// r = seq * G + h' of KV head h (query head h * G + h') take the N side of
+// the MFMA body's products, 16 rows per tile, exactly as a group's heads do
+// in decode.  Wave (row block, chunk, KV head) covers RT row tiles against
+// one chunk of the prefix's tiles and writes one partial per row; the merge
+// adds them to the sequence's own pieces.  Workgroup ids put all row blocks
+// of one (chunk, KV head) on the same XCD, so a tile read by several row
+// blocks is served by that XCD's L2.
+
+template <int D, int BS>
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix(Params p) {
+  using Body = MfmaBody<D, BS, float, false>;   // cached loads: rows blocks re-read tiles
+  using Tile = typename Body::Tile;
+  constexpr int RT = kPrefixRowTiles;
+  __shared__ float p_lds[2][16];
+  const int lane = (int)threadIdx.x;
+  const int c = lane & 15, g = lane >> 4;
+  const int pairs = p.num_kv_heads * p.pf_chunks;
+  const int pair = (int)blockIdx.x % pairs, rb = (int)blockIdx.x / pairs;
+  const int h = pair % p.num_kv_heads, chunk = pair / p.num_kv_heads;
+  const int t_lo = chunk * p.pf_chunk_tiles;
+  const int t_hi = min(t_lo + p.pf_chunk_tiles, p.prefix_tiles);
+  if (t_lo >= t_hi) return;
+  const int R = p.pf_rows;
+
+  typename Body::QRaw q[RT];
+  typename Body::Acc acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int row = min(rb * 16 * RT + t * 16 + c, R - 1);   // rows past R: unused copies
+    const int seq = row / p.group, hq = h * p.group + row % p.group;
+    const bf16_t *qp = static_cast<const bf16_t *>(p.query) + ((int64_t)seq * p.num_q_heads + hq) * D;
+#pragma unroll
+    for (int j = 0; j < Body::QJ; ++j)
+      q[t].c[j] = *reinterpret_cast<const u32x4 *>(qp + (4 * j + g) * 8);
+    Body::init(acc[t]);
+  }
+  const Piece pc{0, 0, t_lo * 16, t_hi * 16, false, false, 0, -1};
+  TableReader tab;
+  tab.start(p, pc, BS);
+  const int64_t head_off = (int64_t)h * D * BS;
+  int lk = t_lo, ck = t_lo;
+  auto load = [&](Tile &tl) -> bool {
+    if (lk >= t_hi) return false;
+    Body::load_tile(p, tab, head_off, lk++, tl);
+    return true;
+  };
+  // One tile against every row tile, as straight-line code: prefix tiles
+  // are always full (no masking) and the rescale is unconditional, so the
+  // RT independent chains (QK^T, softmax, PV) interleave.
+  auto compute = [&](Tile &tl) {
+    mfma_f32x4 sv[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) sv[t] = mfma_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < Body::QJ; ++j)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        sv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(mfma_bf16x8, tl.k[j]), __builtin_bit_cast(mfma_bf16x8, q[t].c[j]),
+            sv[t], 0, 0, 0);
+    mfma_i16x4 pb[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = sv[t][r] * p.scale_log2e;
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float mnew = fmaxf(acc[t].m, mx);
+      const float alpha = fast_exp2(acc[t].m - mnew);
+      acc[t].m = mnew;
+      const unsigned p01 = pack_bf16x2(fast_exp2(sc[0] - mnew), fast_exp2(sc[1] - mnew));
+      const unsigned p23 = pack_bf16x2(fast_exp2(sc[2] - mnew), fast_exp2(sc[3] - mnew));
+      acc[t].lsum = acc[t].lsum * alpha +
+                    ((__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xffff0000u)) +
+                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xffff0000u)));
+#pragma unroll
+      for (int i = 0; i < Body::VT; ++i) acc[t].o[i] *= alpha;
+      pb[t] = __builtin_bit_cast(mfma_i16x4, u32x2{p01, p23});
+    }
+#pragma unroll
+    for (int i = 0; i < Body::VT; ++i)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        acc[t].o[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(mfma_i16x4, tl.v[i]), pb[t], acc[t].o[i], 0, 0, 0);
+    ++ck;
+  };
+  Tile b0, b1;
+  bool h0 = load(b0);
+  bool h1 = load(b1);
+  while (h0) {
+    compute(b0);
+    h0 = load(b0);
+    if (!h1) break;
+    compute(b1);
+    h1 = load(b1);
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float ltot = acc[t].lsum + xor16(acc[t].lsum);
+    ltot += xor32(ltot);
+    const int row = rb * 16 * RT + t * 16 + c;
+    if (row >= R) continue;
+    const int64_t pr = ((int64_t)chunk * p.num_kv_heads + h) * R + row;
+#pragma unroll
+    for (int i = 0; i < Body::VT; ++i)
+      *reinterpret_cast<f32x4 *>(p.pf_acc + pr * D + 16 * i + 4 * g) =
+          f32x4{acc[t].o[i][0], acc[t].o[i][1], acc[t].o[i][2], acc[t].o[i][3]};
+    if (g == 0) {
+      p.pf_max[pr] = acc[t].m;
+      p.pf_sum[pr] = ltot;
+    }
+  }
 }
 
 // ---- log-sum-exp merge -------------------------------------------------------
@@ -1058,36 +1197,58 @@ __global__ __launch_bounds__(64) void decode_merge(Params p) {
       for (int k = 0; k < R; ++k) store_out<OUT>(out + k * 64 + lane, 0.f);
     return;
   }
-  int64_t id0;
-  int n;
+  int64_t id0 = 0;
+  int n = 0;
   if (balanced) {
-    const int64_t g = (int64_t)seq * p.units + unit;
-    const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
-    const int x = unit % p.xsplit, ux = p.units / p.xsplit;
-    n = u1 - u0 + 1;
-    id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
+    if (own_tiles(p, L) > 0) {
+      const int64_t g = (int64_t)seq * p.units + unit;
+      const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
+      const int x = unit % p.xsplit, ux = p.units / p.xsplit;
+      n = u1 - u0 + 1;
+      id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
+    }
   } else {
     n = p.partition_size > 0 ? (L + p.partition_size - 1) / p.partition_size : 1;
     id0 = ((int64_t)seq * p.units + unit) * p.num_partitions;
   }
-  if (n <= 1) return;
+  // The shared prefix's partials of this row: one per chunk, in chunk
+  // order, before the sequence's own pieces.
+  const int npf = p.prefix_tiles > 0 ? p.pf_chunks : 0;
+  const int64_t pf0 = npf ? (int64_t)(qh / p.group) * p.pf_rows + seq * p.group + qh % p.group : 0;
+  const int64_t pf_step = (int64_t)p.num_kv_heads * p.pf_rows;
+  if (npf == 0 && n <= 1) return;
+  const int total = npf + n;
+  auto row_of = [&](int i, const float *&mx, const float *&sm, const float *&ac) {
+    if (i < npf) {
+      const int64_t r = pf0 + i * pf_step;
+      mx = p.pf_max + r; sm = p.pf_sum + r; ac = p.pf_acc + r * D;
+    } else {
+      const int64_t r = (id0 + (i - npf)) * p.gu + hh;
+      mx = p.ws_max + r; sm = p.ws_sum + r; ac = p.ws_acc + r * D;
+    }
+  };
   float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.ws_max[(id0 + i) * p.gu + hh]);
+  for (int i = lane; i < total; i += 64) {
+    const float *mx, *sm, *ac;
+    row_of(i, mx, sm, ac);
+    M = fmaxf(M, *mx);
+  }
   M = wave_max_f(M);
   float den = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const int64_t row = (id0 + i) * p.gu + hh;
-    den += fast_exp2(p.ws_max[row] - M) * p.ws_sum[row];
+  for (int i = lane; i < total; i += 64) {
+    const float *mx, *sm, *ac;
+    row_of(i, mx, sm, ac);
+    den += fast_exp2(*mx - M) * *sm;
   }
   den = wave_sum_f(den);
   float num[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) num[k] = 0.f;
 #pragma unroll 4
-  for (int i = 0; i < n; ++i) {
-    const int64_t row = (id0 + i) * p.gu + hh;
-    const float wgt = fast_exp2(p.ws_max[row] - M);
-    const float *acc = p.ws_acc + row * D;
+  for (int i = 0; i < total; ++i) {
+    const float *mx, *sm, *acc;
+    row_of(i, mx, sm, acc);
+    const float wgt = fast_exp2(*mx - M);
 #pragma unroll
     for (int k = 0; k < R; ++k) num[k] = fmaf(wgt, acc[k * 64 + lane], num[k]);
   }
@@ -1146,6 +1307,34 @@ hipError_t dispatch_out(const DecodeArgs &a, Params &p, bool use_mfma, hipStream
   PA_CASE(128, 32)
   PA_CASE(128, 64)
 #undef PA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix(const DecodeArgs &a, Params &p, hipStream_t st) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const PrefixPlan pf =
+      prefix_plan(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.prefix_len, cus);
+  p.pf_chunks = pf.chunks;
+  p.pf_chunk_tiles = pf.chunk_tiles;
+  p.pf_rows = pf.rows;
+  const int64_t grid = (int64_t)pf.row_blocks * a.num_kv_heads * pf.chunks;
+  if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  const int D = a.head_dim, BS = a.block_size;
+#define PA_PREFIX_CASE(d, bs)                                                              \
+  if (D == d && BS == bs) {                                                                \
+    hipLaunchKernelGGL((decode_prefix<d, bs>), dim3((unsigned)grid), dim3(64), 0, st, p); \
+    return hipGetLastError();                                                              \
+  }
+  PA_PREFIX_CASE(64, 16)
+  PA_PREFIX_CASE(64, 32)
+  PA_PREFIX_CASE(64, 64)
+  PA_PREFIX_CASE(128, 16)
+  PA_PREFIX_CASE(128, 32)
+  PA_PREFIX_CASE(128, 64)
+#undef PA_PREFIX_CASE
   return hipErrorInvalidValue;
 }
 
@@ -1227,9 +1416,18 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.xsplit = 1;
   p.id_stride = 0;
   p.scale_log2e = a.scale * kLog2e;
+  p.prefix_tiles = a.prefix_len / 16;
+  p.pf_chunks = p.pf_chunk_tiles = p.pf_rows = 0;
+  p.pf_max = a.pf_max;
+  p.pf_sum = a.pf_sum;
+  p.pf_acc = a.pf_acc;
   hipError_t e;
   if (a.ev_before_main) {
     e = hipEventRecord(static_cast<hipEvent_t>(a.ev_before_main), st);
+    if (e != hipSuccess) return (int)e;
+  }
+  if (a.prefix_len > 0) {
+    e = launch_prefix(a, p, st);
     if (e != hipSuccess) return (int)e;
   }
   const bool reused = (a.flags & PA_DECODE_KV_REUSED) != 0;

@@ -31,6 +31,8 @@ struct DecodeArgs {
   uint32_t flags;           // PA_DECODE_* bits
   float *ws_max, *ws_sum, *ws_acc;  // split partials, null when every row is written whole
   int32_t *seg_units;               // balanced mode: 2 ints per (sequence, head unit)
+  int32_t prefix_len;               // shared prefix tokens (0: none)
+  float *pf_max, *pf_sum, *pf_acc;  // shared-prefix partials
   int32_t xcd_weights[8];           // balanced mode: relative tile share per XCD
   void *ev_before_main, *ev_after_main;  // optional hipEvent_t pair around the main kernel
 };
@@ -53,6 +55,24 @@ struct BalancedPlan {
 // `resident`: waves the device holds at once for the kernel.
 BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident);
 
+// Shared prefix: its 16-token tiles split into `chunks` runs of
+// `chunk_tiles`, one wave per (row block of kPrefixRowTiles * 16 rows,
+// chunk, KV head); partial rows = chunks * num_kv_heads * rows.
+#ifndef PA_PREFIX_ROW_TILES
+#define PA_PREFIX_ROW_TILES 2
+#endif
+#ifndef PA_PREFIX_WAVES_PER_CU
+#define PA_PREFIX_WAVES_PER_CU 4
+#endif
+constexpr int kPrefixRowTiles = PA_PREFIX_ROW_TILES;     // 16-row tiles per wave
+constexpr int kPrefixWavesPerCU = PA_PREFIX_WAVES_PER_CU;
+struct PrefixPlan {
+  int chunks, chunk_tiles, rows, row_blocks;
+  size_t partial_rows;
+};
+PrefixPlan prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t prefix_len, int cus);
+
 // Current per-XCD weights (pa_set_balance_weights).
 void balance_weights(int32_t out[8]);
 
@@ -60,9 +80,10 @@ void balance_weights(int32_t out[8]);
 // partial rows, each a base-2 max, a sum and head_dim unnormalised outputs,
 // then `segments` pairs of int32 (balanced mode's first/last owning wave).
 struct WorkspaceLayout {
-  size_t rows, max_off, sum_off, acc_off, seg_off, total;
+  size_t rows, max_off, sum_off, acc_off, seg_off, pf_max_off, pf_sum_off, pf_acc_off, total;
 };
-WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments);
+WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments,
+                                 size_t prefix_rows = 0);
 
 // Kernel launchers (pa_decode.hip, pa_cache.hip); they return hipError_t as int.
 int launch_decode(const DecodeArgs &a, void *stream);

@@ -47,6 +47,9 @@ class DecodeStep:
     # reshape_and_cache first (False), or choose by the number of
     # (sequence, KV head) rows written (None).
     fused: Optional[bool] = None
+    # Tokens every sequence shares in the same blocks (0: none); when set,
+    # the attention reads them once for all sequences.
+    prefix_len: int = 0
 
     @property
     def num_pairs(self) -> int:
@@ -63,7 +66,29 @@ class DecodeStep:
                             self.slot_mapping, block_size=self.block_size,
                             num_blocks=self.num_blocks, stream=stream)
 
+    def use_prefix(self, prefix_len: int):
+        """Attend with the shared-prefix kernel from now on (sizing its
+        workspace); the cache write then runs as reshape_and_cache."""
+        import torch
+        self.prefix_len = int(prefix_len)
+        if self.prefix_len:
+            nseq, hq, d = self.query.shape
+            nbytes = B.paged_attention_prefix_workspace_bytes(
+                nseq, hq, self.num_kv_heads, d, self.max_context_len, self.prefix_len,
+                self.query.dtype)
+            self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8,
+                                         device=self.query.device)
+        return self
+
     def attend(self, stream=None, append=False):
+        if self.prefix_len:
+            B.paged_attention_decode_prefix(
+                self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
+                self.context_lens, prefix_len=self.prefix_len, num_kv_heads=self.num_kv_heads,
+                block_size=self.block_size, max_context_len=self.max_context_len,
+                scale=self.scale, workspace=self.workspace, num_blocks=self.num_blocks,
+                stream=stream)
+            return
         extra = dict(new_key=self.new_key, new_value=self.new_value,
                      slot_mapping=self.slot_mapping) if append else {}
         B.paged_attention_decode(self.out, self.query, self.key_cache, self.value_cache,
@@ -84,6 +109,8 @@ class DecodeStep:
 
     @property
     def uses_fused_write(self) -> bool:
+        if self.prefix_len:
+            return False          # the shared-prefix kernel takes no new tokens
         if self.fused is not None:
             return self.fused
         return int(self.query.shape[0]) * self.num_kv_heads <= self.FUSED_MAX_ROWS
@@ -165,11 +192,13 @@ def build_shared_prefix_state(plan) -> "B.BlockAllocator":
     return a
 
 
-def shared_prefix_step(plan, tensors, partition_size: int, out_dtype=None):
+def shared_prefix_step(plan, tensors, partition_size: int, out_dtype=None, prefix=False):
     """The shared-prefix sampling step: fork every sequence into a shadow
     that shares all its blocks (beam-search style), append one token to each
     sequence in ascending id (copy-on-write where the last block is partial
-    and shared), then free the shadows.  Returns (step, host record)."""
+    and shared), then free the shadows.  With prefix=True the attention
+    reads the prompt's full blocks once for all sequences.  Returns (step,
+    host record)."""
     a = build_shared_prefix_state(plan)
     for i in range(plan.batch):
         a.fork(i, SHADOW + i)
@@ -193,5 +222,7 @@ def shared_prefix_step(plan, tensors, partition_size: int, out_dtype=None):
                    scale=tensors["scale"], partition_size=partition_size, out_dtype=out_dtype)
     # The prompt's blocks are shared by every sequence: keep them in the caches.
     step.kv_reused = True
+    if prefix:
+        step.use_prefix(plan.prompt // plan.block_size * plan.block_size)
     record = dict(slots=slots, pairs=pairs, tables=tables, lens=lens32, allocator=a)
     return step, record
