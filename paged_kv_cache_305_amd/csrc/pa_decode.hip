@@ -961,9 +961,28 @@ struct RangePieces {
   int x, ux, seq, k, a, L, n_seq;
   int64_t unit, t, te, id_base;
   LenWindow lens;
+  // A range that starts inside a segment and goes on past it processes that
+  // first piece last: its partial row is then written at the end of the
+  // wave's stream, with the last piece's, instead of in the middle of it
+  // (mid-stream partial writes slow the reads of every wave).
+  Piece deferred;
+  bool has_deferred;
+
+  __device__ void defer_first() {
+    has_deferred = false;
+    if (a > 0 && te - t > n_seq - a) {
+      next(deferred);
+      has_deferred = true;
+    }
+  }
 
   __device__ bool next(Piece &out) {
-    if (t >= te) return false;
+    if (t >= te) {
+      if (!has_deferred) return false;
+      has_deferred = false;
+      out = deferred;
+      return true;
+    }
     const int len = (int)min((int64_t)(n_seq - a), te - t);
     const int b = a + len;
     const int u = x + p->xsplit * k;
@@ -1027,6 +1046,8 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   gen.L = gen.lens.get(p, gen.seq);
   gen.k = (int)((gen.t - seq_first) / gen.n_seq);
   gen.a = (int)((gen.t - seq_first) % gen.n_seq);
+  gen.has_deferred = false;
+  gen.defer_first();
   stream_pieces<Body>(p, gen, p_lds);
 }
 
