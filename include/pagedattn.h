@@ -135,9 +135,9 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
  * caller has reserved it with pa_seq_append_slot, which allocates a block at
  * a block boundary and copies a shared block first; note-023 "Method" and
  * "Concepts").  The wave that loads the 16-token tile holding that position
- * puts the new token into the loaded registers and writes the tile back,
- * so the write costs whole-burst stores instead of a separate pass of
- * scattered ones, and the arithmetic is exactly the unfused pair's.
+ * puts the new token into the loaded registers, so the arithmetic is
+ * exactly the unfused pair's; the slots are written by the launch's waves
+ * after their reads, which saves the separate pass and its launch.
  *
  *  new_key, new_value  [num_seqs][num_kv_heads][head_dim] in kv_dtype (device)
  *  slot_mapping   int64 [num_seqs] (device).  For each i, either negative
@@ -145,10 +145,9 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
  *                 of position context_lens[i] - 1 in block_tables row i,
  *                 in a block that no other sequence of the call reads or
  *                 writes (true of blocks from pa_seq_append_slot, which
- *                 copies a shared block first).  The other tokens of that
- *                 tile are rewritten with the bytes just read from them.
- *                 PA_VALIDATE=1 checks the position; a slot outside the pool
- *                 is skipped like a negative one.
+ *                 copies a shared block first).  PA_VALIDATE=1 checks the
+ *                 position; a slot outside the pool is skipped like a
+ *                 negative one.
  *  Every other argument as in pa_paged_attention_decode (key_cache and
  *  value_cache are written here).
  * ---------------------------------------------------------------------- */

@@ -440,7 +440,8 @@ __device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (
 
 template <typename KV, int D, int BS, typename OUT, bool NT>
 struct ValuBody {
-  static constexpr int kBlockSize = BS;
+  using KVT = KV;
+  static constexpr int kBlockSize = BS, kHeadDim = D;
   static constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
   static constexpr int KJ = D / X / 4;             // key chunks per lane per tile
   static constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
@@ -556,11 +557,9 @@ struct ValuBody {
   }
 
   // Put the appended token (position t1 - 1, lane row r0 of tile kt) into
-  // the loaded tile, as if it had been read from its slot, and -- from one
-  // query head of its group -- store the tile back: the value rows whole
-  // and the keys as the 64-byte runs of four tokens around r0, so every
-  // write covers whole 64-byte memory bursts.
-  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int kt) {
+  // the loaded tile, as if it had been read from its slot.  The slot itself
+  // is written at the end of the launch (store_new_tokens).
+  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int) {
     const int lane = (int)threadIdx.x;
     const int t = lane & 15, g = lane >> 4, vpiece = lane % LPR;
     const int r0 = (pc.t1 - 1) & 15;
@@ -568,9 +567,7 @@ struct ValuBody {
     const int64_t src = ((int64_t)pc.seq * p.num_kv_heads + kvh) * D;
     const KV *nk = static_cast<const KV *>(p.new_key) + src;
     const KV *nv = static_cast<const KV *>(p.new_value) + src;
-    // Every lane loads and selects (no divergent branches): the compiler
-    // then waits once for these loads, and the stores below go out back to
-    // back with their data already in registers.
+    // Every lane loads and selects: no divergent branch around the loads.
     u32x4 kn[KJ];
     KV vn[VJ];
 #pragma unroll
@@ -585,20 +582,6 @@ struct ValuBody {
       const u32x4 w = set_elem<KV>(tl.v[j], r0 % X, vn[j]);
       tl.v[j] = vrow ? w : tl.v[j];
     }
-    if (pc.unit % p.group != 0) return;
-    const int64_t blk = pc.slot / BS;
-    const int sub = (kt * 16) % BS / 16;
-    const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
-    KV *kb = reinterpret_cast<KV *>(p.key_cache) + base + sub * 16 * X;
-    KV *vb = reinterpret_cast<KV *>(p.value_cache) + base + sub * D * 16;
-    if ((t >> 2) == (r0 >> 2)) {
-#pragma unroll
-      for (int j = 0; j < KJ; ++j)
-        *reinterpret_cast<u32x4 *>(kb + ((4 * j + g) * BS + t) * X) = tl.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VJ; ++j)
-      *reinterpret_cast<u32x4 *>(vb + (j * RPI + lane / LPR) * 16 + (lane % LPR) * X) = tl.v[j];
   }
 
   // Combine the sum over the 16 token lanes and each row over its LPR lanes,
@@ -646,7 +629,8 @@ struct ValuBody {
 
 template <int D, int BS, typename OUT, bool NT>
 struct MfmaBody {
-  static constexpr int kBlockSize = BS;
+  using KVT = bf16_t;
+  static constexpr int kBlockSize = BS, kHeadDim = D;
   static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   static constexpr int VT = D / 16;   // 16-feature output tiles
   static constexpr int TPB = BS / 16;
@@ -768,11 +752,9 @@ struct MfmaBody {
   }
 
   // Put the appended token (position t1 - 1, row r0 of tile kt) into the
-  // loaded tile, as if it had been read from its slot, and -- from the
-  // first head tile of its KV head -- store the tile back: the value rows
-  // whole and the keys as the 64-byte runs of four tokens around r0, so
-  // every write covers whole 64-byte memory bursts.
-  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int kt) {
+  // loaded tile, as if it had been read from its slot.  The slot itself is
+  // written at the end of the launch (store_new_tokens).
+  __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int) {
     const int lane = (int)threadIdx.x;
     const int c = lane & 15, g = lane >> 4;
     const int r0 = (pc.t1 - 1) & 15;
@@ -796,20 +778,6 @@ struct MfmaBody {
       const u32x4 w = set_elem<bf16_t>(u32x4{tl.v[i][0], tl.v[i][1], 0u, 0u}, e, vn[i]);
       tl.v[i] = vrow ? u32x2{w[0], w[1]} : tl.v[i];
     }
-    if (pc.unit % p.head_tiles != 0) return;
-    const int64_t blk = pc.slot / BS;
-    const int sub = (kt * 16) % BS / 16;
-    const int64_t base = (blk * p.num_kv_heads + kvh) * (int64_t)D * BS;
-    bf16_t *kb = reinterpret_cast<bf16_t *>(p.key_cache) + base + sub * 16 * 8;
-    bf16_t *vb = reinterpret_cast<bf16_t *>(p.value_cache) + base + sub * D * 16;
-    if ((c >> 2) == (r0 >> 2)) {
-#pragma unroll
-      for (int j = 0; j < QJ; ++j)
-        *reinterpret_cast<u32x4 *>(kb + ((4 * j + g) * BS + c) * 8) = tl.k[j];
-    }
-#pragma unroll
-    for (int i = 0; i < VT; ++i)
-      *reinterpret_cast<u32x2 *>(vb + (16 * i + c) * 16 + 4 * g) = tl.v[i];
   }
 
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
@@ -861,9 +829,40 @@ struct OnePiece {
   }
 };
 
+// The appending variant's cache write: each new token's K and V go into its
+// slot, for every sequence with a slot in the pool, as reshape_and_cache
+// writes them.  No wave of the launch reads these bytes from memory (the
+// tile holding a new token is patched in registers), so the stores wait
+// until the wave has finished its pieces: stores issued between the reads
+// slow the reads of every wave.  Wave w of n stores the (sequence, KV head)
+// pairs j = n - 1 - w, j + n, ...: the last waves to start take the first
+// pairs, so a grid larger than the GPU stores from its last waves.
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
-  __shared__ float p_lds[2][16];
+__device__ __forceinline__ void store_new_tokens(const Params &p, int64_t w, int64_t n) {
+  using KV = typename Body::KVT;
+  constexpr int D = Body::kHeadDim, BS = Body::kBlockSize;
+  constexpr int X = 16 / (int)sizeof(KV);
+  if (p.slots == nullptr) return;
+  const int lane = (int)threadIdx.x;
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  for (int64_t j = n - 1 - w; j < pairs; j += n) {
+    const int seq = (int)(j / p.num_kv_heads);
+    const int64_t slot = p.slots[seq];
+    if (slot < 0 || slot >= p.num_blocks * BS) continue;
+    const int o = (int)(slot % BS);
+    const int64_t base = (slot / BS * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
+    const KV *nk = static_cast<const KV *>(p.new_key) + j * D;
+    const KV *nv = static_cast<const KV *>(p.new_value) + j * D;
+    KV *kc = reinterpret_cast<KV *>(p.key_cache) + base + o * X;
+    KV *vc = reinterpret_cast<KV *>(p.value_cache) + base + (o / 16) * D * 16 + o % 16;
+    for (int c = lane; c < D / X; c += 64)   // key chunk c: x features of the token
+      *reinterpret_cast<u32x4 *>(kc + c * BS * X) = *reinterpret_cast<const u32x4 *>(nk + c * X);
+    for (int e = lane; e < D; e += 64) vc[e * 16] = nv[e];   // value row e of its group
+  }
+}
+
+template <class Body>
+__device__ __forceinline__ void run_fixed(const Params &p, float (&p_lds)[2][16]) {
   int id = (int)blockIdx.x;
   const int unit = id % p.units;
   id /= p.units;
@@ -889,6 +888,13 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
                      ((int64_t)seq * p.units + unit) * p.num_partitions + part, -1},
                false};
   stream_pieces<Body>(p, gen, p_lds);
+}
+
+template <class Body>
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
+  __shared__ float p_lds[2][16];
+  run_fixed<Body>(p, p_lds);
+  store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
 }
 
 // Sum over the wave (all lanes get it).
@@ -947,9 +953,15 @@ struct Split {
     weighted = pp.xsplit == 1 && T * wmin >= cum(wx);
     W = weighted ? wx : (T < wx ? T : wx);
   }
-  // Weighted waves before wave j: sum over v < j of weight[v mod 8].
+  // Weighted waves before wave j: sum over v < j of weight[v mod 8].  The
+  // prefix is picked with selects over constant indices: a runtime index
+  // would copy the array to scratch memory.
   __device__ int64_t cum(int64_t j) const {
-    return (j >> 3) * p->xcd_prefix[8] + p->xcd_prefix[j & 7];
+    const int r = (int)(j & 7);
+    int pre = 0;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) pre = r == i ? p->xcd_prefix[i] : pre;
+    return (j >> 3) * p->xcd_prefix[8] + pre;
   }
   __device__ int64_t begin(int64_t j) const {
     return weighted ? T * cum(j) / cum(W) : T * j / W;
@@ -1012,8 +1024,7 @@ struct RangePieces {
 };
 
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
-  __shared__ float p_lds[2][16];
+__device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16]) {
   const int lane = (int)threadIdx.x;
   RangePieces gen;
   gen.p = &p;
@@ -1049,6 +1060,13 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   gen.has_deferred = false;
   gen.defer_first();
   stream_pieces<Body>(p, gen, p_lds);
+}
+
+template <class Body>
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
+  __shared__ float p_lds[2][16];
+  run_balanced<Body>(p, p_lds);
+  store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
 }
 
 // ---- shared prefix -------------------------------------------------------------

@@ -44,8 +44,8 @@ class DecodeStep:
     partition_size: int
     kv_reused: bool = False
     # Write the new tokens from inside the attention launch (True), with
-    # reshape_and_cache first (False), or choose by the number of
-    # (sequence, KV head) rows written (None).
+    # reshape_and_cache first (False), or from the launch unless the
+    # shared-prefix kernel runs (None).
     fused: Optional[bool] = None
     # Tokens every sequence shares in the same blocks (0: none); when set,
     # the attention reads them once for all sequences.
@@ -99,21 +99,15 @@ class DecodeStep:
                                  num_blocks=self.num_blocks, kv_reused=self.kv_reused,
                                  stream=stream, **extra)
 
-    # The in-launch write stores each new (token, KV head) as whole 64-byte
-    # bursts of the 16-token tile around it (about 5 KiB); on MI355X, with
-    # ~2000 such rows per step (the 7B and 70B-shaped batches) those writes
-    # slow the streaming reads by more than a separate reshape_and_cache
-    # costs, while with a few hundred rows (long contexts, shared prefixes)
-    # the saved launch wins.
-    FUSED_MAX_ROWS = 1024
+    # The in-launch write stores the new tokens after each wave's reads; on
+    # MI355X that costs less than a separate reshape_and_cache pass and its
+    # launch at every batch size measured, so it is the default.
 
     @property
     def uses_fused_write(self) -> bool:
         if self.prefix_len:
             return False          # the shared-prefix kernel takes no new tokens
-        if self.fused is not None:
-            return self.fused
-        return int(self.query.shape[0]) * self.num_kv_heads <= self.FUSED_MAX_ROWS
+        return True if self.fused is None else self.fused
 
     def capture(self):
         """Record run() into a HIP graph (torch.cuda.CUDAGraph); replay()
