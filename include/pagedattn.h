@@ -205,7 +205,9 @@ pa_status pa_set_timing_events(void *before_main, void *after_main);
  * {110,100,110,100,110,100,110,100}: on MI355X, waves on even-numbered XCDs
  * stream about 10% faster than waves on odd-numbered ones.  weights == NULL
  * restores the default; otherwise n must be 8 and each weight in [1, 1000].
- * Process-wide; affects performance only, never results. */
+ * Process-wide.  Weights move the piece boundaries, so outputs may change in
+ * their last bits (within the attention tolerance); for fixed weights,
+ * sizes and lengths every call gives the same bits. */
 pa_status pa_set_balance_weights(const int32_t *weights, int32_t n);
 
 /* Bytes of workspace pa_paged_attention_decode (and _append) needs for these sizes on the

@@ -1196,23 +1196,22 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix(Params p) {
 //
 // One wave per output row (sequence, unit, head in unit).  A row split into
 // pieces with base-2 maxima m_p, sums l_p and unnormalised outputs o_p gets
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// the maxima and sums reduced across lanes, the outputs accumulated in piece
-// order.  Rows of one piece were written whole by the main kernel; in
-// balanced mode this kernel also writes the zero rows of empty sequences.
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Rows of one piece were written whole by the main kernel; in balanced mode
+// this kernel also writes the zero rows of empty sequences.
+//
+// Lanes are (piece group, 4-float chunk of the row): with d = 128, lanes
+// 0-31 take pieces 0, 2, 4, ... and lanes 32-63 pieces 1, 3, 5, ...  Each
+// group folds its pieces in order with an online rescale, four pieces'
+// maxima, sums and outputs requested together, and the groups are combined
+// at the end: a fixed order.  A row of up to 4 * (64 / (d / 4)) pieces per
+// wave costs two dependent memory round trips (its piece range, then the
+// partials); rows with more pieces (long contexts) get a workgroup of NW
+// waves, the groups spread over them and the waves combined through LDS.
 
-__device__ __forceinline__ float wave_max_f(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-template <int D, typename OUT>
-__global__ __launch_bounds__(64) void decode_merge(Params p) {
-  const int lane = (int)threadIdx.x;
+template <int D, typename OUT, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
+  const int lane = (int)threadIdx.x & 63, w = (int)threadIdx.x >> 6;
   int r = (int)blockIdx.x;
   const int hh = r % p.gu;
   r /= p.gu;
@@ -1226,14 +1225,16 @@ __global__ __launch_bounds__(64) void decode_merge(Params p) {
     if (h >= p.group) return;
     qh = (unit / p.head_tiles) * p.group + h;
   }
-  constexpr int R = D / 64;
+  constexpr int CH = D / 4;      // 4-float chunks per row
+  constexpr int PG = 64 / CH;    // piece groups per wave
+  constexpr int GT = PG * NW;    // piece groups in the workgroup
+  constexpr int KB = 4;          // pieces per group whose loads are issued together
+  const int ch = lane % CH, pg = lane / CH;
   OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + qh) * D;
   const int L = seq_len(p, seq);
   const bool balanced = p.partition_size < 0;
   if (L == 0) {
-    if (balanced)
-#pragma unroll
-      for (int k = 0; k < R; ++k) store_out<OUT>(out + k * 64 + lane, 0.f);
+    if (balanced && w == 0 && pg == 0) store_out4<OUT>(out + 4 * ch, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   int64_t id0 = 0;
@@ -1266,34 +1267,80 @@ __global__ __launch_bounds__(64) void decode_merge(Params p) {
       mx = p.ws_max + r; sm = p.ws_sum + r; ac = p.ws_acc + r * D;
     }
   };
-  float M = -INFINITY;
-  for (int i = lane; i < total; i += 64) {
-    const float *mx, *sm, *ac;
-    row_of(i, mx, sm, ac);
-    M = fmaxf(M, *mx);
-  }
-  M = wave_max_f(M);
-  float den = 0.f;
-  for (int i = lane; i < total; i += 64) {
-    const float *mx, *sm, *ac;
-    row_of(i, mx, sm, ac);
-    den += fast_exp2(*mx - M) * *sm;
-  }
-  den = wave_sum_f(den);
-  float num[R];
+  // Each lane group folds its pieces in order with an online rescale
+  // (running max mg, sum sg, output ag), KB pieces' loads at a time.
+  float mg = -INFINITY, sg = 0.f;
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = w * PG + pg; i0 < total; i0 += GT * KB) {
+    float pm[KB], ps[KB];
+    f32x4 po[KB];
 #pragma unroll
-  for (int k = 0; k < R; ++k) num[k] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < total; ++i) {
-    const float *mx, *sm, *acc;
-    row_of(i, mx, sm, acc);
-    const float wgt = fast_exp2(*mx - M);
+    for (int j = 0; j < KB; ++j) {
+      const int i = i0 + GT * j;
+      pm[j] = -INFINITY;
+      ps[j] = 0.f;
+      po[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < total) {
+        const float *mx, *sm, *ac;
+        row_of(i, mx, sm, ac);
+        pm[j] = *mx;
+        ps[j] = *sm;
+        po[j] = *reinterpret_cast<const f32x4 *>(ac + 4 * ch);
+      }
+    }
 #pragma unroll
-    for (int k = 0; k < R; ++k) num[k] = fmaf(wgt, acc[k * 64 + lane], num[k]);
+    for (int j = 0; j < KB; ++j) {
+      if (i0 + GT * j < total) {
+        const float mn = fmaxf(mg, pm[j]);
+        const float a = fast_exp2(mg - mn), b = fast_exp2(pm[j] - mn);
+        ag = ag * a + po[j] * b;
+        sg = sg * a + ps[j] * b;
+        mg = mn;
+      }
+    }
+  }
+  // Combine the wave's groups: M over its pieces, each group's share
+  // rescaled to it; then the waves in order.
+  float M = mg;
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float f = mg == -INFINITY ? 0.f : fast_exp2(mg - M);
+  f32x4 acc = ag * f;
+  float den = sg * f;
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1) {
+    acc[0] += __shfl_xor(acc[0], off);
+    acc[1] += __shfl_xor(acc[1], off);
+    acc[2] += __shfl_xor(acc[2], off);
+    acc[3] += __shfl_xor(acc[3], off);
+    den += __shfl_xor(den, off);
+  }
+  if constexpr (NW > 1) {
+    __shared__ f32x4 s_acc[NW][CH];
+    __shared__ float s_m[NW], s_den[NW];
+    if (pg == 0) {
+      s_acc[w][ch] = acc;
+      if (ch == 0) {
+        s_m[w] = M;
+        s_den[w] = den;
+      }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = s_m[0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) Mt = fmaxf(Mt, s_m[k]);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    den = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float fk = s_m[k] == -INFINITY ? 0.f : fast_exp2(s_m[k] - Mt);
+      acc += s_acc[k][ch] * fk;
+      den += s_den[k] * fk;
+    }
   }
   const float inv = 1.f / den;
-#pragma unroll
-  for (int k = 0; k < R; ++k) store_out<OUT>(out + k * 64 + lane, num[k] * inv);
+  if (pg == 0) store_out4<OUT>(out + 4 * ch, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
 // ---- dispatch ----------------------------------------------------------------
@@ -1377,15 +1424,41 @@ hipError_t launch_prefix(const DecodeArgs &a, Params &p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Waves per output row for the merge: enough that each wave's piece groups
+// get at most one batch of loads for the pieces a row is expected to have
+// (balanced split: a segment spans about waves / segments ranges, plus one
+// for the cuts; fixed partitions: the longest sequence's count).
+template <int D>
+int merge_waves(const DecodeArgs &a, const Params &p) {
+  constexpr int per_wave = 4 * (64 / (D / 4));
+  int64_t est;
+  if (a.partition_size < 0) {
+    const int64_t segs = (int64_t)a.num_seqs * (p.units / p.xsplit);
+    est = segs > 0 ? (p.waves / p.xsplit + segs - 1) / segs + 1 : 1;
+  } else {
+    est = a.num_partitions;
+  }
+  if (a.prefix_len > 0) est += p.pf_chunks;
+  return est > 2 * per_wave ? 4 : est > per_wave ? 2 : 1;
+}
+
+template <int D, typename OUT>
+hipError_t launch_merge_d(const Params &p, int64_t rows, int nw, hipStream_t st) {
+  if (nw == 4)
+    hipLaunchKernelGGL((decode_merge<D, OUT, 4>), dim3((unsigned)rows), dim3(256), 0, st, p);
+  else if (nw == 2)
+    hipLaunchKernelGGL((decode_merge<D, OUT, 2>), dim3((unsigned)rows), dim3(128), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_merge<D, OUT, 1>), dim3((unsigned)rows), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
 template <typename OUT>
 hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
   const int64_t rows = (int64_t)a.num_seqs * p.units * p.gu;
   if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL((decode_merge<64, OUT>), dim3((unsigned)rows), dim3(64), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_merge<128, OUT>), dim3((unsigned)rows), dim3(64), 0, st, p);
-  return hipGetLastError();
+  if (a.head_dim == 64) return launch_merge_d<64, OUT>(p, rows, merge_waves<64>(a, p), st);
+  return launch_merge_d<128, OUT>(p, rows, merge_waves<128>(a, p), st);
 }
 
 }  // namespace

@@ -132,6 +132,16 @@ def test_old_contents_of_the_new_slots_are_never_read(gpu):
             assert torch.equal(out, clean)
 
 
+@pytest.mark.parametrize("name,batch", [("7b", 64), ("70b", 128)])
+def test_more_new_tokens_than_waves(gpu, name, batch):
+    """Short contexts keep the balanced grid small (a few tiles per wave), so
+    each wave stores the new tokens of several (sequence, KV head) pairs
+    after its pieces."""
+    lens = tuple(1 + (7 * i) % 16 for i in range(batch))
+    case = W.make_case(name, device="cuda", batch=batch, lens=lens)
+    _check_case(gpu, case, BAL)
+
+
 def test_full_size_steps_on_sampled_sequences(gpu):
     for name in ("7b", "70b"):
         case = W.make_case(name, device="cuda")

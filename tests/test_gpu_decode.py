@@ -49,6 +49,10 @@ SMALL = [
     ("7b", dict(batch=4, len_range=(1, 200), head_dim=64, num_q_heads=4, num_kv_heads=4)),
     ("tiny", dict(num_q_heads=8, num_kv_heads=2, lens=(5, 40, 64, 129), pool=40)),  # fp32 GQA
     ("tiny", dict(head_dim=128, block_size=32, lens=(1, 31, 33, 90))),
+    # The balanced split's set-up holds up to 512 lengths in registers and
+    # walks larger batches chunk by chunk: one case on each side.
+    ("7b", dict(batch=512, len_range=(1, 40), num_q_heads=4, num_kv_heads=4)),
+    ("70b", dict(batch=520, len_range=(1, 48))),
 ]
 
 
