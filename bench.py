@@ -8,7 +8,7 @@ on the GPU copy_blocks on those pairs, and the attention over all cached
 tokens (main kernel, plus the log-sum-exp merge when a sequence spans
 several pieces).  Each sequence's new token is written into its slot either
 by that launch or by reshape_and_cache just before it (--cache-write; by
-default the launch writes, except with the shared-prefix kernel).
+default the launch writes).
 
 Timing: W warm-up steps, then K timed steps.  Before each step a 1 GiB
 buffer is read to evict the L2s and the Infinity Cache (outside the
@@ -327,8 +327,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--cache-write", choices=["auto", "fused", "separate"], default="auto",
                     help="write the new tokens inside the attention launch (fused), with "
-                         "reshape_and_cache before it (separate), or fused where the "
-                         "kernel takes them (auto)")
+                         "reshape_and_cache before it (separate); auto = fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--block-size", type=int, default=None,

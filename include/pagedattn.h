@@ -172,12 +172,20 @@ pa_status pa_paged_attention_decode_append(
  *  prefix_len     positive multiple of block_size, <= every context_lens[i];
  *                 block_tables rows agree on their first prefix_len /
  *                 block_size entries (PA_VALIDATE=1 checks both).
+ *  new_key, new_value, slot_mapping
+ *                 all NULL, or the step's new tokens exactly as in
+ *                 pa_paged_attention_decode_append (written by this call).
+ *                 A new token sits after the prefix (context_lens[i] >
+ *                 prefix_len where slot_mapping[i] >= 0): its block is the
+ *                 sequence's own.  PA_VALIDATE=1 checks this too.
  *  workspace      pa_paged_attention_prefix_workspace_bytes(...) bytes.
  *  Needs bf16 K/V (PA_ERR_UNSUPPORTED otherwise); other arguments as in
  *  pa_paged_attention_decode, with the balanced split.
  * ---------------------------------------------------------------------- */
-pa_status pa_paged_attention_decode_prefix(void *out, const void *query, const void *key_cache,
-                                           const void *value_cache, const int32_t *block_tables,
+pa_status pa_paged_attention_decode_prefix(void *out, const void *query, void *key_cache,
+                                           void *value_cache, const void *new_key,
+                                           const void *new_value, const int64_t *slot_mapping,
+                                           const int32_t *block_tables,
                                            const int32_t *context_lens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,

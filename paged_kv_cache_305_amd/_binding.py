@@ -69,9 +69,9 @@ def _declare(lib):
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
-        "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
-                                                   i32, i32, i64, i32, f32, i32, i32, i32,
-                                                   ctypes.c_uint32, vp, sz, vp]),
+        "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                   i32, i32, i32, i32, i64, i32, f32, i32, i32,
+                                                   i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_prefix_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_set_timing_events": (i32, [vp, vp]),
         "pa_set_balance_weights": (i32, [vp, i32]),
@@ -246,13 +246,33 @@ def paged_attention_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, 
         _dtype_code_of(kv_dtype)))
 
 
+def _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, dtype, dev):
+    """Device pointers of a step's new tokens (all three given) or zeros (none)."""
+    if new_key is None and new_value is None and slot_mapping is None:
+        return 0, 0, 0
+    if new_key is None or new_value is None or slot_mapping is None:
+        raise ValueError("new_key, new_value and slot_mapping go together")
+    for t, n in ((new_key, "new_key"), (new_value, "new_value"), (slot_mapping, "slot_mapping")):
+        _dev(t, n, dev)
+    if tuple(new_key.shape) != (B, num_kv_heads, d) or new_value.shape != new_key.shape:
+        raise ValueError("new_key and new_value must be [num_seqs, num_kv_heads, head_dim]")
+    if new_key.dtype != dtype or new_value.dtype != dtype:
+        raise TypeError("new_key and new_value must have the pools' dtype")
+    if slot_mapping.dtype != _torch().int64 or slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be int64 [num_seqs]")
+    return new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr()
+
+
 def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tables,
                                   context_lens, *, prefix_len: int, num_kv_heads: int,
                                   block_size: int, max_context_len: int, scale: float,
                                   workspace=None, num_blocks: Optional[int] = None,
+                                  new_key=None, new_value=None, slot_mapping=None,
                                   stream=None):
     """Decode attention when every sequence's first prefix_len tokens are the
-    same physical blocks (sequence 0's): those are read once for all rows."""
+    same physical blocks (sequence 0's): those are read once for all rows.
+    new_key, new_value and slot_mapping as in paged_attention_decode (each
+    new token after the prefix)."""
     lib = load()
     dev = query.device
     for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
@@ -266,12 +286,13 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
     if tuple(out.shape) != (B, hq, d):
         raise ValueError("out must have the query's shape")
     nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev)
     need = paged_attention_prefix_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
                                                   prefix_len, query.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(lib.pa_paged_attention_decode_prefix(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *news,
         block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
         int(block_tables.shape[1]), nb, int(max_context_len), float(scale), int(prefix_len),
         _dtype_code(query), _dtype_code(out), 0, _dev(workspace, "workspace", dev).data_ptr(),
@@ -315,18 +336,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     chunk = num_kv_heads * d * block_size
     if key_cache.numel() < nb * chunk or value_cache.numel() < nb * chunk:
         raise ValueError("pools hold fewer than num_blocks blocks")
-    if appending:
-        if new_key is None or new_value is None or slot_mapping is None:
-            raise ValueError("new_key, new_value and slot_mapping go together")
-        for t, n in ((new_key, "new_key"), (new_value, "new_value"),
-                     (slot_mapping, "slot_mapping")):
-            _dev(t, n, dev)
-        if tuple(new_key.shape) != (B, num_kv_heads, d) or new_value.shape != new_key.shape:
-            raise ValueError("new_key and new_value must be [num_seqs, num_kv_heads, head_dim]")
-        if new_key.dtype != query.dtype or new_value.dtype != query.dtype:
-            raise TypeError("new_key and new_value must have the pools' dtype")
-        if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (B,):
-            raise ValueError("slot_mapping must be int64 [num_seqs]")
+    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev)
     need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
                                            partition_size, query.dtype)
     if need and workspace is None:
@@ -340,7 +350,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     if appending:
         _check(lib.pa_paged_attention_decode_append(
             out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-            new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(), *tail))
+            *news, *tail))
     else:
         _check(lib.pa_paged_attention_decode(
             out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),

@@ -304,6 +304,9 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
           return pa_fail(PA_ERR_INVALID_ARG, "%s: slot_mapping[%d] = %lld is not the slot of "
                          "position context_lens - 1 (%lld)", fn, i, (long long)slots[i],
                          (long long)want);
+        if (pos < prefix_len)
+          return pa_fail(PA_ERR_INVALID_ARG, "%s: sequence %d appends at position %d, inside "
+                         "the shared prefix", fn, i, pos);
       }
     }
   }
@@ -370,8 +373,10 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                      workspace, workspace_bytes, stream);
 }
 
-pa_status pa_paged_attention_decode_prefix(void *out, const void *query, const void *key_cache,
-                                           const void *value_cache, const int32_t *block_tables,
+pa_status pa_paged_attention_decode_prefix(void *out, const void *query, void *key_cache,
+                                           void *value_cache, const void *new_key,
+                                           const void *new_value, const int64_t *slot_mapping,
+                                           const int32_t *block_tables,
                                            const int32_t *context_lens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,
@@ -384,7 +389,7 @@ pa_status pa_paged_attention_decode_prefix(void *out, const void *query, const v
   const char *fn = "pa_paged_attention_decode_prefix";
   if (prefix_len <= 0)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: prefix_len must be positive", fn);
-  return decode_call(fn, out, query, key_cache, value_cache, nullptr, nullptr, nullptr,
+  return decode_call(fn, out, query, key_cache, value_cache, new_key, new_value, slot_mapping,
                      block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                      PA_PARTITION_BALANCED, kv_dtype, out_dtype, flags, workspace,

@@ -43,9 +43,8 @@ class DecodeStep:
     scale: float
     partition_size: int
     kv_reused: bool = False
-    # Write the new tokens from inside the attention launch (True), with
-    # reshape_and_cache first (False), or from the launch unless the
-    # shared-prefix kernel runs (None).
+    # Write the new tokens from inside the attention launch (True or None,
+    # the default) or with reshape_and_cache first (False).
     fused: Optional[bool] = None
     # Tokens every sequence shares in the same blocks (0: none); when set,
     # the attention reads them once for all sequences.
@@ -68,7 +67,7 @@ class DecodeStep:
 
     def use_prefix(self, prefix_len: int):
         """Attend with the shared-prefix kernel from now on (sizing its
-        workspace); the cache write then runs as reshape_and_cache."""
+        workspace)."""
         import torch
         self.prefix_len = int(prefix_len)
         if self.prefix_len:
@@ -81,16 +80,16 @@ class DecodeStep:
         return self
 
     def attend(self, stream=None, append=False):
+        extra = dict(new_key=self.new_key, new_value=self.new_value,
+                     slot_mapping=self.slot_mapping) if append else {}
         if self.prefix_len:
             B.paged_attention_decode_prefix(
                 self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
                 self.context_lens, prefix_len=self.prefix_len, num_kv_heads=self.num_kv_heads,
                 block_size=self.block_size, max_context_len=self.max_context_len,
                 scale=self.scale, workspace=self.workspace, num_blocks=self.num_blocks,
-                stream=stream)
+                stream=stream, **extra)
             return
-        extra = dict(new_key=self.new_key, new_value=self.new_value,
-                     slot_mapping=self.slot_mapping) if append else {}
         B.paged_attention_decode(self.out, self.query, self.key_cache, self.value_cache,
                                  self.block_tables, self.context_lens,
                                  num_kv_heads=self.num_kv_heads, block_size=self.block_size,
@@ -105,8 +104,6 @@ class DecodeStep:
 
     @property
     def uses_fused_write(self) -> bool:
-        if self.prefix_len:
-            return False          # the shared-prefix kernel takes no new tokens
         return True if self.fused is None else self.fused
 
     def capture(self):
