@@ -432,9 +432,8 @@ def main():
     achieved = attn_bytes / t_main / 1e9
     body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
                           step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
-    kernel = "%s<%s>" % ("decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
-    if step.prefix_len:
-        kernel = "decode_prefix + " + kernel
+    kernel = "%s<%s>" % ("decode_prefix_tails" if step.prefix_len else
+                         "decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
     roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=counter_traffic(args.workload, args.partition_size),

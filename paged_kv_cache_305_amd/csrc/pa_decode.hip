@@ -46,6 +46,8 @@
 // exponentiated with v_exp_f32; the stored partition maxima are base-2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -231,11 +233,13 @@ struct Params {
   float scale_log2e;
   // Shared prefix (0 tiles when unused): every sequence's first
   // prefix_tiles * 16 tokens are the same physical blocks, those of
-  // sequence 0.  decode_prefix covers them for all query rows at once and
-  // the balanced split only the tiles after them.
+  // sequence 0.  The prefix waves (run_prefix) cover them for all query
+  // rows at once and the balanced split only the tiles after them.
   int prefix_tiles;
   int pf_chunks, pf_chunk_tiles;   // prefix split into chunks of tiles
   int pf_rows;                     // query rows per KV head: num_seqs * group
+  int pf_waves;                    // prefix waves of the launch
+  int pf_mix;                      // tail / prefix waves dealt alternately, per kind
   float *pf_max, *pf_sum, *pf_acc; // partials [chunk][KV head][row]
 };
 
@@ -442,6 +446,7 @@ template <typename KV, int D, int BS, typename OUT, bool NT>
 struct ValuBody {
   using KVT = KV;
   static constexpr int kBlockSize = BS, kHeadDim = D;
+  static constexpr bool kStreams = NT;
   static constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
   static constexpr int KJ = D / X / 4;             // key chunks per lane per tile
   static constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
@@ -631,6 +636,7 @@ template <int D, int BS, typename OUT, bool NT>
 struct MfmaBody {
   using KVT = bf16_t;
   static constexpr int kBlockSize = BS, kHeadDim = D;
+  static constexpr bool kStreams = NT;
   static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   static constexpr int VT = D / 16;   // 16-feature output tiles
   static constexpr int TPB = BS / 16;
@@ -1023,13 +1029,16 @@ struct RangePieces {
   }
 };
 
+// vb: the wave's index in the split (its workgroup id, or its place among
+// the tail waves of a shared-prefix launch; vb and the workgroup id agree
+// mod 8, so the wave runs on XCD vb mod 8).
 template <class Body>
-__device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16]) {
+__device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16], int vb) {
   const int lane = (int)threadIdx.x;
   RangePieces gen;
   gen.p = &p;
-  gen.x = (int)blockIdx.x % p.xsplit;
-  gen.unit = (int64_t)blockIdx.x / p.xsplit;
+  gen.x = vb % p.xsplit;
+  gen.unit = (int64_t)vb / p.xsplit;
   gen.ux = p.units / p.xsplit;
   const Split sp(p, tiles_per_unit(p));
   if (gen.unit >= sp.W) return;
@@ -1065,7 +1074,7 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
 template <class Body>
 __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
   __shared__ float p_lds[2][16];
-  run_balanced<Body>(p, p_lds);
+  run_balanced<Body>(p, p_lds, (int)blockIdx.x);
   store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
 }
 
@@ -1079,20 +1088,20 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
 // the MFMA body's products, 16 rows per tile, exactly as a group's heads do
 // in decode.  Wave (row block, chunk, KV head) covers RT row tiles against
 // one chunk of the prefix's tiles and writes one partial per row; the merge
-// adds them to the sequence's own pieces.  Workgroup ids put all row blocks
-// of one (chunk, KV head) on the same XCD, so a tile read by several row
+// adds them to the sequence's own pieces.  Wave ids put all row blocks of
+// one (chunk, KV head) on the same XCD, so a tile read by several row
 // blocks is served by that XCD's L2.
 
+// vb: the wave's index among the launch's prefix waves.
 template <int D, int BS>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix(Params p) {
+__device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16], int vb) {
   using Body = MfmaBody<D, BS, float, false>;   // cached loads: rows blocks re-read tiles
   using Tile = typename Body::Tile;
   constexpr int RT = kPrefixRowTiles;
-  __shared__ float p_lds[2][16];
   const int lane = (int)threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
   const int pairs = p.num_kv_heads * p.pf_chunks;
-  const int pair = (int)blockIdx.x % pairs, rb = (int)blockIdx.x / pairs;
+  const int pair = vb % pairs, rb = vb / pairs;
   const int h = pair % p.num_kv_heads, chunk = pair / p.num_kv_heads;
   const int t_lo = chunk * p.pf_chunk_tiles;
   const int t_hi = min(t_lo + p.pf_chunk_tiles, p.prefix_tiles);
@@ -1189,6 +1198,33 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix(Params p) {
       p.pf_max[pr] = acc[t].m;
       p.pf_sum[pr] = ltot;
     }
+  }
+}
+
+// Shared prefix and per-sequence tails in one launch: prefix waves wait on
+// cache-level reads of the few prefix blocks, tail waves stream the
+// sequences' own blocks from HBM, so the two kinds overlap.  Workgroups are
+// dealt in runs of 8, alternating tail / prefix while both kinds remain,
+// then the rest of the larger kind; each wave's index within its kind
+// equals its workgroup id mod 8, which keeps both kinds' XCD placement.
+template <class Body>
+__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix_tails(Params p) {
+  __shared__ float p_lds[2][16];
+  const int b = (int)blockIdx.x, m = p.pf_mix;
+  bool tail;
+  int vb;
+  if (b < 2 * m) {
+    tail = ((b >> 3) & 1) == 0;
+    vb = ((b >> 4) << 3) | (b & 7);
+  } else {
+    tail = p.waves > p.pf_waves;
+    vb = m + (b - 2 * m);
+  }
+  if (tail) {
+    run_balanced<Body>(p, p_lds, vb);
+    store_new_tokens<Body>(p, vb, p.waves);
+  } else {
+    run_prefix<Body::kHeadDim, Body::kBlockSize>(p, p_lds, vb);
   }
 }
 
@@ -1356,18 +1392,45 @@ int resident_waves(const void *kernel) {
   return cus * per_cu;
 }
 
+// The balanced split, alone or (shared prefix) with the prefix waves: the
+// tails then get the resident waves the prefix waves leave.
+template <class Body>
+hipError_t launch_balanced(const DecodeArgs &a, Params &p, hipStream_t st) {
+  const bool pf = p.prefix_tiles > 0;
+  constexpr bool pf_ok = std::is_same<typename Body::KVT, bf16_t>::value && Body::kStreams;
+  if (pf && !pf_ok) return hipErrorInvalidValue;   // prefix calls are bf16 and stream their tails
+  const void *k = reinterpret_cast<const void *>(&decode_balanced<Body>);
+  if constexpr (pf_ok) {
+    if (pf) k = reinterpret_cast<const void *>(&decode_prefix_tails<Body>);
+  }
+  int resident = resident_waves(k);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  if (pf) resident = resident - p.pf_waves > 64 ? resident - p.pf_waves : 64;
+  const BalancedPlan plan = balanced_plan(a, p.units, resident);
+  if (plan.waves <= 0) return hipErrorInvalidDevice;
+  p.waves = plan.waves;
+  p.xsplit = plan.xsplit;
+  p.id_stride = plan.id_stride;
+  p.xcd_prefix[0] = 0;
+  for (int i = 0; i < 8; ++i) p.xcd_prefix[i + 1] = p.xcd_prefix[i] + a.xcd_weights[i];
+  if constexpr (pf_ok) {
+    if (pf) {
+      const int m = plan.waves < p.pf_waves ? plan.waves : p.pf_waves;
+      p.pf_mix = m - m % 8;
+      const int64_t grid = (int64_t)plan.waves + p.pf_waves;
+      if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((decode_prefix_tails<Body>), dim3((unsigned)grid), dim3(64), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_balanced<Body>), dim3(plan.waves), dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
 template <class Body, typename OUT>
 hipError_t launch_body(const DecodeArgs &a, Params &p, hipStream_t st) {
   if (p.partition_size < 0) {
-    const void *k = reinterpret_cast<const void *>(&decode_balanced<Body>);
-    const BalancedPlan plan = balanced_plan(a, p.units, resident_waves(k));
-    if (plan.waves <= 0) return hipErrorInvalidDevice;
-    p.waves = plan.waves;
-    p.xsplit = plan.xsplit;
-    p.id_stride = plan.id_stride;
-    p.xcd_prefix[0] = 0;
-    for (int i = 0; i < 8; ++i) p.xcd_prefix[i + 1] = p.xcd_prefix[i] + a.xcd_weights[i];
-    hipLaunchKernelGGL((decode_balanced<Body>), dim3(plan.waves), dim3(64), 0, st, p);
+    return launch_balanced<Body>(a, p, st);
   } else {
     const int64_t grid = (int64_t)p.units * a.num_seqs * p.num_partitions;
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
@@ -1396,7 +1459,9 @@ hipError_t dispatch_out(const DecodeArgs &a, Params &p, bool use_mfma, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefix(const DecodeArgs &a, Params &p, hipStream_t st) {
+// The shared prefix's plan: chunks of the prefix and the waves that cover
+// them, launched with the tails by launch_balanced.
+hipError_t plan_prefix(const DecodeArgs &a, Params &p) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1407,21 +1472,9 @@ hipError_t launch_prefix(const DecodeArgs &a, Params &p, hipStream_t st) {
   p.pf_chunk_tiles = pf.chunk_tiles;
   p.pf_rows = pf.rows;
   const int64_t grid = (int64_t)pf.row_blocks * a.num_kv_heads * pf.chunks;
-  if (grid <= 0 || grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  const int D = a.head_dim, BS = a.block_size;
-#define PA_PREFIX_CASE(d, bs)                                                              \
-  if (D == d && BS == bs) {                                                                \
-    hipLaunchKernelGGL((decode_prefix<d, bs>), dim3((unsigned)grid), dim3(64), 0, st, p); \
-    return hipGetLastError();                                                              \
-  }
-  PA_PREFIX_CASE(64, 16)
-  PA_PREFIX_CASE(64, 32)
-  PA_PREFIX_CASE(64, 64)
-  PA_PREFIX_CASE(128, 16)
-  PA_PREFIX_CASE(128, 32)
-  PA_PREFIX_CASE(128, 64)
-#undef PA_PREFIX_CASE
-  return hipErrorInvalidValue;
+  if (grid <= 0 || grid > INT32_MAX / 2) return hipErrorInvalidConfiguration;
+  p.pf_waves = (int)grid;
+  return hipSuccess;
 }
 
 // Waves per output row for the merge: enough that each wave's piece groups
@@ -1475,7 +1528,8 @@ BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident) {
   const int64_t t_upper = (int64_t)units * a.num_seqs * tiles_max;
   const int64_t cap = (t_upper + kMinTiles - 1) / kMinTiles;
   if (cap < w) w = cap > 0 ? (int)cap : 1;
-  pl.xsplit = ((a.flags & PA_DECODE_KV_REUSED) && units % 8 == 0 && w >= 64) ? 8 : 1;
+  pl.xsplit = ((a.flags & PA_DECODE_KV_REUSED) && a.prefix_len == 0 && units % 8 == 0 && w >= 64)
+                  ? 8 : 1;
   if (w >= 8) w -= w % 8;   // whole rounds of the 8 XCDs
   w -= w % pl.xsplit;
   pl.waves = w;
@@ -1529,7 +1583,7 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.id_stride = 0;
   p.scale_log2e = a.scale * kLog2e;
   p.prefix_tiles = a.prefix_len / 16;
-  p.pf_chunks = p.pf_chunk_tiles = p.pf_rows = 0;
+  p.pf_chunks = p.pf_chunk_tiles = p.pf_rows = p.pf_waves = p.pf_mix = 0;
   p.pf_max = a.pf_max;
   p.pf_sum = a.pf_sum;
   p.pf_acc = a.pf_acc;
@@ -1539,10 +1593,12 @@ int launch_decode(const DecodeArgs &a, void *stream) {
     if (e != hipSuccess) return (int)e;
   }
   if (a.prefix_len > 0) {
-    e = launch_prefix(a, p, st);
+    e = plan_prefix(a, p);
     if (e != hipSuccess) return (int)e;
   }
-  const bool reused = (a.flags & PA_DECODE_KV_REUSED) != 0;
+  // With a shared prefix the reused blocks are the prefix's, read by the
+  // prefix waves; the tails are streamed.
+  const bool reused = (a.flags & PA_DECODE_KV_REUSED) != 0 && a.prefix_len == 0;
   if (a.out_dtype == PA_BF16)
     e = reused ? dispatch_out<bf16_t, false>(a, p, hu.mfma, st)
                : dispatch_out<bf16_t, true>(a, p, hu.mfma, st);
