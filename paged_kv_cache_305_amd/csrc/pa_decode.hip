@@ -447,6 +447,7 @@ struct ValuBody {
   using KVT = KV;
   static constexpr int kBlockSize = BS, kHeadDim = D;
   static constexpr bool kStreams = NT;
+  static constexpr int kWavesPerEU = sizeof(KV) == 4 && D == 128 ? 1 : 2;
   static constexpr int X = 16 / (int)sizeof(KV);   // elements per 16-byte chunk
   static constexpr int KJ = D / X / 4;             // key chunks per lane per tile
   static constexpr int LPR = (int)sizeof(KV);      // lanes per 16-token value row
@@ -637,6 +638,7 @@ struct MfmaBody {
   using KVT = bf16_t;
   static constexpr int kBlockSize = BS, kHeadDim = D;
   static constexpr bool kStreams = NT;
+  static constexpr int kWavesPerEU = 2;
   static constexpr int QJ = D / 32;   // 16x16x32 steps over the features
   static constexpr int VT = D / 16;   // 16-feature output tiles
   static constexpr int TPB = BS / 16;
@@ -816,9 +818,12 @@ struct MfmaBody {
 
 // ---- grid strategies ---------------------------------------------------------
 
-// Two waves per SIMD at least: a single resident wave cannot keep enough
-// bytes in flight.
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(2)))
+// Waves per SIMD the body is compiled for (Body::kWavesPerEU): two, so that
+// enough bytes are in flight; one for fp32 K/V at d = 128, whose two 16 KiB
+// tile buffers and query registers do not fit in half the register file
+// (at two it spilled ~300 bytes per lane to scratch) and which keeps the
+// same bytes in flight per CU with one.
+#define PA_OCCUPANCY(Body) __attribute__((amdgpu_waves_per_eu(Body::kWavesPerEU)))
 
 // Fixed partitions: workgroup id -> (unit, sequence, partition), the unit
 // varying fastest.  Consecutive workgroups go round-robin to the 8 XCDs, so
@@ -897,7 +902,7 @@ __device__ __forceinline__ void run_fixed(const Params &p, float (&p_lds)[2][16]
 }
 
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_fixed(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_fixed(Params p) {
   __shared__ float p_lds[2][16];
   run_fixed<Body>(p, p_lds);
   store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
@@ -1072,7 +1077,7 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
 }
 
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_balanced(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_balanced(Params p) {
   __shared__ float p_lds[2][16];
   run_balanced<Body>(p, p_lds, (int)blockIdx.x);
   store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
@@ -1208,7 +1213,7 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
 // then the rest of the larger kind; each wave's index within its kind
 // equals its workgroup id mod 8, which keeps both kinds' XCD placement.
 template <class Body>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void decode_prefix_tails(Params p) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_prefix_tails(Params p) {
   __shared__ float p_lds[2][16];
   const int b = (int)blockIdx.x, m = p.pf_mix;
   bool tail;
