@@ -39,6 +39,13 @@
 //    is instead done per XCD: 8 sub-problems, units u = x (mod 8) on waves
 //    w = x (mod 8), so each KV head's blocks stay in one XCD's L2.
 //
+// Appending calls (the step's new tokens given): the wave that loads the
+// tile holding a sequence's last position puts the new token into its
+// registers, and every wave stores a share of the new tokens into their
+// slots after its pieces.  Shared-prefix calls: prefix waves read the common
+// blocks once per KV head for all query rows, tail waves run the balanced
+// split over each sequence's own tiles, both kinds in one launch.
+//
 // Every reduction order is fixed by logical token position, so results are
 // deterministic and independent of where the blocks sit physically.
 //
