@@ -57,13 +57,13 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def build_step(name, ps, device, block_size=None, table_order="random", prefix=True):
+def build_step(name, ps, device, block_size=None, table_order="random", prefix=True, batch=None):
     import workloads as W
     from paged_kv_cache_305_amd.step import shared_prefix_step, step_from_case
     if name == "shared":
         if table_order != "random":
             raise SystemExit("the shared-prefix tables come from the allocator")
-        plan = W.shared_plan(block_size=block_size)
+        plan = W.shared_plan(block_size=block_size, batch=batch)
         tens = W.shared_tensors(plan, device=device)
         step, rec = shared_prefix_step(plan, tens, partition_size=ps, prefix=prefix)
         lens = rec["lens"].astype(np.int64)
@@ -71,7 +71,10 @@ def build_step(name, ps, device, block_size=None, table_order="random", prefix=T
                                 num_blocks=plan.num_blocks, block_size=plan.block_size)
     base = "long" if name == "long32" else name
     bs = block_size or (32 if name == "long32" else None)
-    case = W.make_case(base, device=device, **(dict(block_size=bs) if bs else {}))
+    over = dict(block_size=bs) if bs else {}
+    if batch:
+        over["batch"] = batch
+    case = W.make_case(base, device=device, **over)
     if table_order == "identity":
         # Contiguous storage: each sequence's blocks are consecutive physical
         # blocks, sequences one after another.
@@ -325,6 +328,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per split-K partition; 0 = none, -1 = balanced split")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="sequences in the step (default: the workload's); lengths keep the "
+                         "workload's distribution")
     ap.add_argument("--cache-write", choices=["auto", "fused", "separate"], default="auto",
                     help="write the new tokens inside the attention launch (fused), with "
                          "reshape_and_cache before it (separate); auto = fused")
@@ -374,7 +380,7 @@ def main():
     log("building workload %s" % args.workload)
     step, lens, info = build_step(args.workload, args.partition_size, device,
                                   block_size=args.block_size, table_order=args.table_order,
-                                  prefix=not args.no_prefix)
+                                  prefix=not args.no_prefix, batch=args.batch)
     step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
@@ -452,7 +458,9 @@ def main():
         "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[step.query.dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block permutation)",
-        "config": {"workload": WORKLOADS[args.workload], "partition_size": args.partition_size,
+        "config": {"workload": WORKLOADS[args.workload] + (
+                       " (batch set to %d)" % B if args.batch else ""),
+                   "partition_size": args.partition_size,
                    "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
                    "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
                    "shared_prefix_tokens": step.prefix_len,

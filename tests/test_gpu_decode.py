@@ -95,6 +95,15 @@ def test_full_size_workloads_on_sampled_sequences(gpu, name, kw, ps):
     _check(gpu, case, ps, idx=idx)
 
 
+@pytest.mark.parametrize("ps", [BAL, 512])
+def test_a_quarter_million_token_context(gpu, ps):
+    """One sequence of 262,144 tokens (1 GiB of bf16 K/V for 8 KV heads): the
+    balanced split cuts each of its 8 segments into ~256 pieces, so the merge
+    runs its 4-wave workgroups through many load batches."""
+    case = W.make_case("long", device="cuda", lens=(262144,), batch=1)
+    _check(gpu, case, ps)
+
+
 @pytest.mark.parametrize("name,kw", [("7b", dict(batch=6, len_range=(1, 3000))),
                                      ("70b", dict(batch=6, len_range=(1, 3000))),
                                      ("7b", dict(batch=4, len_range=(1, 200), num_q_heads=16,

@@ -179,8 +179,8 @@ def case_structure(name: str, *, batch: Optional[int] = None, seed: Optional[int
         lengths = rng.integers(lo, hi + 1, size=b).astype(np.int64)
     else:
         lengths = np.asarray(cfg["lens"], dtype=np.int64)
-        if batch is not None:
-            lengths = lengths[:batch]
+        if batch is not None:   # the fixed lengths, cycled or cut to the batch
+            lengths = np.resize(lengths, batch)
     needed = int(sum(blocks_for(l, bs) for l in lengths))
     pool = cfg["pool"] if pool is None else pool
     if pool == "1.5x":
