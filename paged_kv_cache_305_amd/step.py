@@ -5,8 +5,9 @@ block at a block boundary and returning a (src, dst) copy pair when the
 last block is shared (copy-on-write).  Device, in stream order: copy_blocks
 on the pairs, then the attention over every sequence's cached tokens with
 the new tokens written into their slots by the same launch
-(paged_attention_decode_append) -- or, unfused, reshape_and_cache followed
-by paged_attention_decode.  Both give the same pools and outputs.
+(paged_attention_decode_append, or paged_attention_decode_prefix when the
+sequences share a prefix) -- or, unfused, reshape_and_cache followed by the
+attention.  Both give the same pools and outputs.
 
 The host part runs once when the step is built; ``run()`` only launches the
 kernels, so it can be repeated (same pairs, same slots, same reads) for
