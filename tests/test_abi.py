@@ -82,6 +82,37 @@ def test_append_needs_all_three_new_token_pointers():
     assert lib.pa_paged_attention_decode_append(*a.values()) == pa.PA_OK
 
 
+def _prefix(lib, **kw):
+    a = dict(out=16, query=32, key_cache=48, value_cache=64, new_key=NULL, new_value=NULL,
+             slot_mapping=NULL, block_tables=8, context_lens=8, num_seqs=2, num_q_heads=8,
+             num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4,
+             num_blocks=16, max_context_len=64, scale=0.1, prefix_len=32,
+             kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16, flags=0, workspace=NULL,
+             workspace_bytes=0, stream=NULL)
+    a.update(kw)
+    return lib.pa_paged_attention_decode_prefix(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(new_key=80), pa.PA_ERR_INVALID_ARG),                                # not all three
+    (dict(new_key=80, new_value=96), pa.PA_ERR_INVALID_ARG),
+    (dict(new_key=80, new_value=104, slot_mapping=8), pa.PA_ERR_INVALID_ARG),  # misaligned
+    (dict(prefix_len=0), pa.PA_ERR_INVALID_ARG),
+    (dict(prefix_len=24), pa.PA_ERR_INVALID_ARG),                             # not a block multiple
+    (dict(prefix_len=80), pa.PA_ERR_INVALID_ARG),                             # > max_context_len
+    (dict(kv_dtype=pa.PA_FP32, out_dtype=pa.PA_FP32), pa.PA_ERR_UNSUPPORTED),
+])
+def test_prefix_call_rejects_bad_arguments_before_launch(kw, status):
+    lib = pa.load()
+    assert _prefix(lib, **kw) == status
+    assert lib.pa_last_error()
+
+
+def test_prefix_call_with_no_sequences_is_a_no_op():
+    lib = pa.load()
+    assert _prefix(lib, num_seqs=0, new_key=80, new_value=96, slot_mapping=8) == pa.PA_OK
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     lib = pa.load()
     assert _decode(lib, num_seqs=0) == pa.PA_OK
