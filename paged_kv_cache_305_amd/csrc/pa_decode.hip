@@ -158,6 +158,20 @@ __device__ __forceinline__ void store_out4<bf16_t>(bf16_t *p, float a, float b, 
 
 // ---- cross-lane ------------------------------------------------------------
 
+// Lane within the wave.  Every routine below works on one wave; workgroups
+// of several waves (the merge, the shared-prefix launch) are built from them.
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
+
+// Orders this wave's LDS writes before its following LDS reads of other
+// lanes' values: an exchange within one wave needs no workgroup barrier (a
+// wave's LDS operations complete in order), only that the compiler keep the
+// order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -173,7 +187,7 @@ __device__ __forceinline__ float xor16(float v) {
 }
 // Lane l gets the value of lane l ^ 32.
 __device__ __forceinline__ float xor32(float v) {
-  const int src = (int)(threadIdx.x ^ 32u) << 2;
+  const int src = (lane_id() ^ 32) << 2;
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
 }
 
@@ -302,7 +316,7 @@ struct TableReader {
   int chunk, vals, vals_next;
 
   __device__ __forceinline__ int fetch(int c) const {
-    const int idx = (c << 6) + (int)threadIdx.x;
+    const int idx = (c << 6) + lane_id();
     return idx < count ? row[first + idx] : 0;
   }
 
@@ -335,7 +349,7 @@ struct LenWindow {
   int base, vals;
   __device__ __forceinline__ void load(const Params &p, int b) {
     base = b;
-    const int i = b + (int)threadIdx.x;
+    const int i = b + lane_id();
     vals = i < p.num_seqs ? seq_len(p, i) : 0;
   }
   __device__ __forceinline__ int get(const Params &p, int seq) {
@@ -480,7 +494,7 @@ struct ValuBody {
 
   __device__ static void zero_rows(const Params &p, int seq, int unit) {
     OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + unit) * D;
-    for (int d = (int)threadIdx.x; d < D; d += 64) store_out<OUT>(out + d, 0.f);
+    for (int d = lane_id(); d < D; d += 64) store_out<OUT>(out + d, 0.f);
   }
 
   __device__ static int64_t head_offset(const Params &p, int unit) {
@@ -489,7 +503,7 @@ struct ValuBody {
 
   // The lane's key chunks c = 4j + g of query head `unit`.
   __device__ static void load_q(const Params &p, const Piece &pc, QRaw &q) {
-    const int g = (int)threadIdx.x >> 4;
+    const int g = lane_id() >> 4;
     const KV *qp =
         static_cast<const KV *>(p.query) + ((int64_t)pc.seq * p.num_q_heads + pc.unit) * D;
 #pragma unroll
@@ -506,7 +520,7 @@ struct ValuBody {
 
   __device__ static void load_tile(const Params &p, TableReader &tab, int64_t head_off, int kt,
                                    Tile &tl) {
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int t = lane & 15, g = lane >> 4;
     const int blk = kt / TPB, sub = kt % TPB;
     const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
@@ -531,7 +545,7 @@ struct ValuBody {
   __device__ static void compute(const Params &p, const Piece &pc, const QReady &q, Acc &a,
                                  Tile &tl, int kt, float (&p_lds)[2][16]) {
     if (appends_in(pc, kt)) patch_tile(p, pc, tl, kt);
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int t = lane & 15, vpiece = lane % LPR;
     float dot = 0.f;
 #pragma unroll
@@ -552,7 +566,7 @@ struct ValuBody {
     a.m = mnew;
     const int buf = kt & 1;
     if (lane < 16) p_lds[buf][t] = pr;
-    __syncthreads();
+    wave_lds_sync();
     if (kt * 16 + 16 > pc.t1) {  // ragged last tile: unwritten slots may hold NaN
 #pragma unroll
       for (int j = 0; j < VJ; ++j)
@@ -573,7 +587,7 @@ struct ValuBody {
   // the loaded tile, as if it had been read from its slot.  The slot itself
   // is written at the end of the launch (store_new_tokens).
   __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int) {
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int t = lane & 15, g = lane >> 4, vpiece = lane % LPR;
     const int r0 = (pc.t1 - 1) & 15;
     const int kvh = pc.unit / p.group;
@@ -600,7 +614,7 @@ struct ValuBody {
   // Combine the sum over the 16 token lanes and each row over its LPR lanes,
   // then write the output row or the partial.
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int vrow = lane / LPR;
     const float ltot = row16_sum(a.lsum);
 #pragma unroll
@@ -665,11 +679,11 @@ struct MfmaBody {
 
   // Head of the group this lane's column holds, and whether it exists.
   __device__ static int group_head(const Params &p, int unit) {
-    return (unit % p.head_tiles) * 16 + ((int)threadIdx.x & 15);
+    return (unit % p.head_tiles) * 16 + (lane_id() & 15);
   }
 
   __device__ static void zero_rows(const Params &p, int seq, int unit) {
-    const int g = (int)threadIdx.x >> 4;
+    const int g = lane_id() >> 4;
     const int h = group_head(p, unit);
     if (h >= p.group) return;
     OUT *out = static_cast<OUT *>(p.out) +
@@ -683,7 +697,7 @@ struct MfmaBody {
   }
 
   __device__ static void load_q(const Params &p, const Piece &pc, QRaw &q) {
-    const int g = (int)threadIdx.x >> 4;
+    const int g = lane_id() >> 4;
     const int h = group_head(p, pc.unit);
     const int qh = (pc.unit / p.head_tiles) * p.group + (h < p.group ? h : 0);
     const bf16_t *qp = static_cast<const bf16_t *>(p.query) +
@@ -702,7 +716,7 @@ struct MfmaBody {
 
   __device__ static void load_tile(const Params &p, TableReader &tab, int64_t head_off, int kt,
                                    Tile &tl) {
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int c = lane & 15, g = lane >> 4;
     const int blk = kt / TPB, sub = kt % TPB;
     const int64_t base = (int64_t)tab.phys(blk, p.num_blocks) * p.num_kv_heads * D * BS + head_off;
@@ -724,7 +738,7 @@ struct MfmaBody {
   __device__ static void compute(const Params &p, const Piece &pc, const QReady &q, Acc &a,
                                  Tile &tl, int kt, float (&)[2][16]) {
     if (appends_in(pc, kt)) patch_tile(p, pc, tl, kt);
-    const int g = (int)threadIdx.x >> 4;
+    const int g = lane_id() >> 4;
     mfma_f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < QJ; ++j)
@@ -770,7 +784,7 @@ struct MfmaBody {
   // loaded tile, as if it had been read from its slot.  The slot itself is
   // written at the end of the launch (store_new_tokens).
   __device__ static void patch_tile(const Params &p, const Piece &pc, Tile &tl, int) {
-    const int lane = (int)threadIdx.x;
+    const int lane = lane_id();
     const int c = lane & 15, g = lane >> 4;
     const int r0 = (pc.t1 - 1) & 15;
     const int kvh = pc.unit / p.head_tiles;
@@ -796,7 +810,7 @@ struct MfmaBody {
   }
 
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
-    const int g = (int)threadIdx.x >> 4, hh = (int)threadIdx.x & 15;
+    const int g = lane_id() >> 4, hh = lane_id() & 15;
     float ltot = a.lsum + xor16(a.lsum);
     ltot += xor32(ltot);
     const int h = group_head(p, pc.unit);
@@ -861,7 +875,7 @@ __device__ __forceinline__ void store_new_tokens(const Params &p, int64_t w, int
   constexpr int D = Body::kHeadDim, BS = Body::kBlockSize;
   constexpr int X = 16 / (int)sizeof(KV);
   if (p.slots == nullptr) return;
-  const int lane = (int)threadIdx.x;
+  const int lane = lane_id();
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
   for (int64_t j = n - 1 - w; j < pairs; j += n) {
     const int seq = (int)(j / p.num_kv_heads);
@@ -923,7 +937,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 // Inclusive prefix sum over the wave's lanes.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = (int)threadIdx.x & 63;
+  const int lane = lane_id();
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(v, off);
     if (lane >= off) v += y;
@@ -935,7 +949,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
   int64_t tot = 0;
   for (int c = 0; c < p.num_seqs; c += 64) {
-    const int i = c + ((int)threadIdx.x & 63);
+    const int i = c + lane_id();
     tot += wave_sum(i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0);
   }
   return tot;
@@ -1017,7 +1031,7 @@ struct RangePieces {
     const int b = a + len;
     const int u = x + p->xsplit * k;
     const int64_t g = (int64_t)seq * p->units + u;
-    if (threadIdx.x == 0) {
+    if (lane_id() == 0) {
       if (a == 0) p->seg_units[2 * g] = (int32_t)unit;
       if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
     }
@@ -1046,7 +1060,7 @@ struct RangePieces {
 // mod 8, so the wave runs on XCD vb mod 8).
 template <class Body>
 __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16], int vb) {
-  const int lane = (int)threadIdx.x;
+  const int lane = lane_id();
   RangePieces gen;
   gen.p = &p;
   gen.x = vb % p.xsplit;
@@ -1110,7 +1124,7 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
   using Body = MfmaBody<D, BS, float, false>;   // cached loads: rows blocks re-read tiles
   using Tile = typename Body::Tile;
   constexpr int RT = kPrefixRowTiles;
-  const int lane = (int)threadIdx.x;
+  const int lane = lane_id();
   const int c = lane & 15, g = lane >> 4;
   const int pairs = p.num_kv_heads * p.pf_chunks;
   const int pair = vb % pairs, rb = vb / pairs;
