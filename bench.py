@@ -215,13 +215,15 @@ def counter_traffic(workload, ps):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(step, lens, max_seconds):
+def cpu_baseline(step, lens, max_seconds, threads=None):
     """The oracle, as it stands, on this host's cores, over a bounded sample:
     consecutive sequences of the step (wrapping around the batch), in chunks
-    that double while they fit, until about max_seconds of wall time."""
+    that double while they fit, until about max_seconds of wall time.
+    threads: default min(16, cores of this host)."""
     import oracle
     import workloads as W
-    threads = max(1, min(16, os.cpu_count() or 1))
+    if threads is None:
+        threads = max(1, min(16, os.cpu_count() or 1))
     kc = W.host_array(step.key_cache)
     vc = W.host_array(step.value_cache)
     q = W.host_array(step.query)
@@ -502,8 +504,12 @@ def main():
                            "value_GBs": round(kv_bytes / (float(np.mean(g_ms)) / 1e3) / 1e9, 1)}
         log("graph replay: step %.1f us" % (float(np.mean(g_ms)) * 1e3))
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ~%.0f s" % args.cpu_seconds)
+        log("cpu baseline (oracle) ~%.0f s, then ~%.0f s on one thread" % (
+            args.cpu_seconds, args.cpu_seconds / 3))
         result["cpu_baseline"] = cpu_baseline(step, lens, args.cpu_seconds)
+        one = cpu_baseline(step, lens, args.cpu_seconds / 3, threads=1)
+        result["cpu_baseline"]["single_thread"] = {
+            k: one[k] for k in ("value", "unit", "tokens_per_s", "seconds", "sample")}
     print(json.dumps(result), flush=True)
 
 
