@@ -1405,6 +1405,94 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
   if (pg == 0) store_out4<OUT>(out + 4 * ch, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
+// Merge of a balanced split's MFMA head units when segments have few pieces
+// (many sequences): one wave per segment (sequence, unit) merges all of the
+// unit's rows, so the launch has gu times fewer waves than one per row and
+// reads the segment's owning waves once.  Lanes are (four-float chunk ch,
+// row group rg); row group rg owns the rows hh = rg + RGN * r, r < RG, and
+// folds each over its pieces in position order (online rescale), KB pieces'
+// loads for all of its rows at a time.
+template <int D, typename OUT, int RG>
+__global__ __launch_bounds__(64) void decode_merge_units(Params p) {
+  constexpr int CH = D / 4;      // 4-float chunks per row
+  constexpr int RGN = 64 / CH;   // row groups per wave
+  constexpr int KB = 2;          // pieces per row whose loads are issued together
+  const int lane = lane_id();
+  const int ch = lane % CH, rg = lane / CH;
+  const int64_t g = (int64_t)blockIdx.x;   // seq * units + unit
+  const int unit = (int)(g % p.units);
+  const int seq = (int)(g / p.units);
+  const int h0 = (unit % p.head_tiles) * 16;   // the unit's first head within its group
+  const int nh = min(p.gu, p.group - h0);      // rows the unit holds
+  OUT *out = static_cast<OUT *>(p.out) +
+             ((int64_t)seq * p.num_q_heads + (unit / p.head_tiles) * p.group + h0) * D + 4 * ch;
+  const int L = seq_len(p, seq);
+  if (L == 0) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int hh = rg + RGN * r;
+      if (hh < nh) store_out4<OUT>(out + (int64_t)hh * D, 0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  if (own_tiles(p, L) == 0) return;
+  const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
+  const int n = u1 - u0 + 1;
+  if (n <= 1) return;   // one piece: the main kernel wrote the rows
+  const int x = unit % p.xsplit, ux = p.units / p.xsplit;
+  const int64_t id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
+  float mg[RG], sg[RG];
+  f32x4 ag[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    mg[r] = -INFINITY;
+    sg[r] = 0.f;
+    ag[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i0 = 0; i0 < n; i0 += KB) {
+    float pm[KB][RG], ps[KB][RG];
+    f32x4 po[KB][RG];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int hh = rg + RGN * r;
+        pm[j][r] = -INFINITY;
+        ps[j][r] = 0.f;
+        po[j][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (i0 + j < n && hh < nh) {
+          const int64_t row = (id0 + i0 + j) * p.gu + hh;
+          pm[j][r] = p.ws_max[row];
+          ps[j][r] = p.ws_sum[row];
+          po[j][r] = *reinterpret_cast<const f32x4 *>(p.ws_acc + row * D + 4 * ch);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (i0 + j < n) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const float mn = fmaxf(mg[r], pm[j][r]);
+          const float a = fast_exp2(mg[r] - mn), b = fast_exp2(pm[j][r] - mn);
+          ag[r] = ag[r] * a + po[j][r] * b;
+          sg[r] = sg[r] * a + ps[j][r] * b;
+          mg[r] = mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int hh = rg + RGN * r;
+    if (hh < nh) {
+      const float inv = 1.f / sg[r];
+      store_out4<OUT>(out + (int64_t)hh * D, ag[r][0] * inv, ag[r][1] * inv, ag[r][2] * inv,
+                      ag[r][3] * inv);
+    }
+  }
+}
+
 // ---- dispatch ----------------------------------------------------------------
 
 // Waves of `kernel` the device holds at once (64-thread workgroups).
@@ -1503,6 +1591,11 @@ hipError_t plan_prefix(const DecodeArgs &a, Params &p) {
   return hipSuccess;
 }
 
+// Expected pieces per segment up to which a balanced split's MFMA units are
+// merged one wave per segment (decode_merge_units folds a row's pieces two
+// loads at a time, so more pieces mean more dependent rounds).
+constexpr int64_t kUnitMergeMaxPieces = 4;
+
 // Waves per output row for the merge: enough that each wave's piece groups
 // get at most one batch of loads for the pieces a row is expected to have
 // (balanced split: a segment spans about waves / segments ranges, plus one
@@ -1532,10 +1625,37 @@ hipError_t launch_merge_d(const Params &p, int64_t rows, int nw, hipStream_t st)
   return hipGetLastError();
 }
 
+template <int D, typename OUT>
+hipError_t launch_merge_units_d(const Params &p, int64_t segs, hipStream_t st) {
+  constexpr int RGN = 64 / (D / 4);
+  const int rg = (p.gu + RGN - 1) / RGN;
+  const dim3 grid((unsigned)segs);
+  if (rg <= 1)
+    hipLaunchKernelGGL((decode_merge_units<D, OUT, 1>), grid, dim3(64), 0, st, p);
+  else if (rg <= 2)
+    hipLaunchKernelGGL((decode_merge_units<D, OUT, 2>), grid, dim3(64), 0, st, p);
+  else if (rg <= 4)
+    hipLaunchKernelGGL((decode_merge_units<D, OUT, 4>), grid, dim3(64), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_merge_units<D, OUT, 8>), grid, dim3(64), 0, st, p);
+  return hipGetLastError();
+}
+
 template <typename OUT>
 hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
   const int64_t rows = (int64_t)a.num_seqs * p.units * p.gu;
   if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
+  // Balanced split of MFMA units (several rows per segment) with few pieces
+  // per segment: one wave per segment.
+  if (a.partition_size < 0 && a.prefix_len == 0 && p.gu > 1) {
+    const int64_t segs = (int64_t)a.num_seqs * p.units;
+    const int64_t sx = (int64_t)a.num_seqs * (p.units / p.xsplit);
+    const int64_t est = sx > 0 ? (p.waves / p.xsplit + sx - 1) / sx + 1 : 1;
+    if (est <= kUnitMergeMaxPieces) {
+      if (a.head_dim == 64) return launch_merge_units_d<64, OUT>(p, segs, st);
+      return launch_merge_units_d<128, OUT>(p, segs, st);
+    }
+  }
   if (a.head_dim == 64) return launch_merge_d<64, OUT>(p, rows, merge_waves<64>(a, p), st);
   return launch_merge_d<128, OUT>(p, rows, merge_waves<128>(a, p), st);
 }

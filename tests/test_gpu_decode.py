@@ -69,6 +69,29 @@ def test_small_cases_match_oracle(gpu, name, kw, ps):
     _check(gpu, case, ps)
 
 
+# Many short sequences give the balanced split about one piece per segment
+# of the MFMA body, whose rows are then merged one wave per segment: every
+# row-group count (d 128: 2 row groups, d 64: 4), a partly filled second head
+# tile, and empty sequences.
+UNIT_MERGE = [
+    dict(num_q_heads=8, num_kv_heads=4),                  # G 2
+    dict(num_q_heads=32, num_kv_heads=8),                 # G 4
+    dict(num_q_heads=64, num_kv_heads=8),                 # G 8
+    dict(num_q_heads=16, num_kv_heads=1),                 # G 16: 8 rows per row group
+    dict(num_q_heads=40, num_kv_heads=2),                 # G 20: second head tile has 4 rows
+    dict(num_q_heads=24, num_kv_heads=8, head_dim=64),    # G 3, d 64
+    dict(num_q_heads=64, num_kv_heads=4, head_dim=64),    # G 16, d 64
+]
+
+
+@pytest.mark.parametrize("kw", UNIT_MERGE)
+def test_many_short_sequences_merged_per_segment(gpu, kw):
+    case = W.make_case("70b", device="cuda", batch=300, len_range=(0, 90), **kw)
+    assert (case.context_lens == 0).any() and (case.context_lens > 64).any()
+    for od in (torch.float32, torch.bfloat16):
+        _check(gpu, case, BAL, out_dtype=od)
+
+
 @pytest.mark.parametrize("name,kw", [("7b", dict(batch=3, len_range=(1, 300))),
                                      ("70b", dict(batch=3, len_range=(1, 300))),
                                      ("tiny", {})])
