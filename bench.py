@@ -362,6 +362,7 @@ def main():
 
     import torch
     import paged_kv_cache_305_amd as pa
+    import workloads as W
     if args.waste_report:
         for row in waste_report():
             print(json.dumps(row), flush=True)
@@ -444,7 +445,13 @@ def main():
                          "decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
     roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                traffic=counter_traffic(args.workload, args.partition_size),
+                # The committed counters were taken on the workload as it
+                # stands (its own block size, batch and placement, default
+                # cache write and prefix use): any other variant gets none.
+                traffic=counter_traffic(args.workload, args.partition_size)
+                if args.block_size in (None, W.CONFIGS[args.workload]["block_size"]) and args.batch is None
+                and args.table_order == "random" and args.cache_write == "auto"
+                and not args.no_prefix else None,
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
                 kernel_source_digest=kernel_source_digest())
     result = {
