@@ -100,15 +100,17 @@ void balance_weights(int32_t out[8]) {
   for (int i = 0; i < 8; ++i) out[i] = g_xcd_weights[i].load(std::memory_order_relaxed);
 }
 
-WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments,
+WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments, size_t waves,
                                  size_t prefix_rows) {
-  WorkspaceLayout w{rows, 0, 0, 0, 0, 0, 0, 0, 0};
+  WorkspaceLayout w{rows, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (rows == 0 && prefix_rows == 0) return w;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.sum_off = up(rows * sizeof(float));
   w.acc_off = w.sum_off + up(rows * sizeof(float));
   w.seg_off = w.acc_off + up(rows * (size_t)head_dim * sizeof(float));
-  w.pf_max_off = w.seg_off + up(segments * 2 * sizeof(int32_t));
+  w.cnt_off = w.seg_off + up(segments * 2 * sizeof(int32_t));
+  w.wave_off = w.cnt_off + up(segments * sizeof(int32_t));
+  w.pf_max_off = w.wave_off + up(waves * sizeof(int32_t));
   w.pf_sum_off = w.pf_max_off + up(prefix_rows * sizeof(float));
   w.pf_acc_off = w.pf_sum_off + up(prefix_rows * sizeof(float));
   w.total = w.pf_acc_off + up(prefix_rows * (size_t)head_dim * sizeof(float));
@@ -174,7 +176,8 @@ size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
   if (partition_size < 0 && bound == 0) return 0;
   return pa::workspace_layout(
              partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
-             partition_size < 0 ? (size_t)num_seqs * hu.units : 0)
+             partition_size < 0 ? (size_t)num_seqs * hu.units : 0,
+             partition_size < 0 ? (size_t)bound : 0)
       .total;
 }
 
@@ -249,7 +252,8 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                                             bound / 32);
   const pa::WorkspaceLayout ws = pa::workspace_layout(
       partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
-      partition_size < 0 ? (size_t)num_seqs * hu.units : 0, pf.partial_rows);
+      partition_size < 0 ? (size_t)num_seqs * hu.units : 0,
+      partition_size < 0 ? (size_t)bound : 0, pf.partial_rows);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu", fn,
@@ -341,6 +345,8 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
   a.ws_sum = ws.total ? reinterpret_cast<float *>(wsb + ws.sum_off) : nullptr;
   a.ws_acc = ws.total ? reinterpret_cast<float *>(wsb + ws.acc_off) : nullptr;
   a.seg_units = ws.total ? reinterpret_cast<int32_t *>(wsb + ws.seg_off) : nullptr;
+  a.seg_cnt = ws.total ? reinterpret_cast<int32_t *>(wsb + ws.cnt_off) : nullptr;
+  a.wave_segs = ws.total ? reinterpret_cast<int32_t *>(wsb + ws.wave_off) : nullptr;
   a.prefix_len = prefix_len;
   a.pf_max = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_max_off) : nullptr;
   a.pf_sum = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_sum_off) : nullptr;
@@ -410,7 +416,7 @@ size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q
   const pa::PrefixPlan pf = pa::prefix_plan(num_seqs, num_q_heads, num_kv_heads, prefix_len,
                                             bound / 32);
   return pa::workspace_layout(partial_rows(num_seqs, hu, max_context_len, -1, bound), head_dim,
-                              (size_t)num_seqs * hu.units, pf.partial_rows)
+                              (size_t)num_seqs * hu.units, (size_t)bound, pf.partial_rows)
       .total;
 }
 

@@ -239,6 +239,8 @@ struct Params {
   const int64_t *slots;
   float *ws_max, *ws_sum, *ws_acc;   // partial rows: [piece * gu + head in unit]
   int32_t *seg_units;                // balanced: per segment, first and last owning wave
+  int32_t *seg_cnt;                  // balanced: per segment, chunks merged so far (merge)
+  int32_t *wave_segs;                // balanced: per wave, the segment its range starts in
   int64_t num_blocks;
   int num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, max_context_len;
   int partition_size;   // > 0 fixed partitions, 0 whole segments, < 0 balanced
@@ -1004,6 +1006,7 @@ struct RangePieces {
   const Params *p;
   int x, ux, seq, k, a, L, n_seq;
   int64_t unit, t, te, id_base;
+  int64_t first_g;           // segment holding the range's first tile (-1: none)
   LenWindow lens;
   // A range that starts inside a segment and goes on past it processes that
   // first piece last: its partial row is then written at the end of the
@@ -1032,7 +1035,10 @@ struct RangePieces {
     const int u = x + p->xsplit * k;
     const int64_t g = (int64_t)seq * p->units + u;
     if (lane_id() == 0) {
-      if (a == 0) p->seg_units[2 * g] = (int32_t)unit;
+      if (a == 0) {
+        p->seg_units[2 * g] = (int32_t)unit;
+        if (p->seg_cnt) p->seg_cnt[g] = 0;   // the merge counts this segment's chunks
+      }
       if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
     }
     const int pt = p->prefix_tiles;
@@ -1066,8 +1072,16 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   gen.x = vb % p.xsplit;
   gen.unit = (int64_t)vb / p.xsplit;
   gen.ux = p.units / p.xsplit;
+  gen.first_g = -1;
+  // The wave's record for the merge: the segment its range starts in.
+  auto record = [&]() {
+    if (p.wave_segs != nullptr && lane == 0) p.wave_segs[vb] = (int32_t)gen.first_g;
+  };
   const Split sp(p, tiles_per_unit(p));
-  if (gen.unit >= sp.W) return;
+  if (gen.unit >= sp.W) {
+    record();
+    return;
+  }
   gen.t = sp.begin(gen.unit);
   gen.te = sp.begin(gen.unit + 1);
   gen.id_base = (int64_t)gen.x * p.id_stride;
@@ -1087,13 +1101,18 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
     }
     base += __builtin_amdgcn_readlane(incl, 63);
   }
-  if (gen.seq < 0) return;   // unreachable while t < T
+  if (gen.seq < 0) {   // unreachable while t < T
+    record();
+    return;
+  }
   gen.lens.load(p, gen.seq);
   gen.L = gen.lens.get(p, gen.seq);
   gen.k = (int)((gen.t - seq_first) / gen.n_seq);
   gen.a = (int)((gen.t - seq_first) % gen.n_seq);
+  gen.first_g = (int64_t)gen.seq * p.units + gen.x + p.xsplit * gen.k;
   gen.has_deferred = false;
   gen.defer_first();
+  record();
   stream_pieces<Body>(p, gen, p_lds);
 }
 
@@ -1405,90 +1424,189 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
   if (pg == 0) store_out4<OUT>(out + 4 * ch, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
 }
 
-// Merge of a balanced split's MFMA head units when segments have few pieces
-// (many sequences): one wave per segment (sequence, unit) merges all of the
-// unit's rows, so the launch has gu times fewer waves than one per row and
-// reads the segment's owning waves once.  Lanes are (four-float chunk ch,
-// row group rg); row group rg owns the rows hh = rg + RGN * r, r < RG, and
-// folds each over its pieces in position order (online rescale), KB pieces'
-// loads for all of its rows at a time.
+// ---- merge of the balanced split, many sequences -----------------------------
+//
+// Used when segments are expected to span few pieces (many sequences: each
+// wave's range holds about one segment).  A segment split over the main
+// kernel's waves u0..u1 (n = u1 - u0 + 1 pieces, consecutive piece ids) has
+// its pieces grouped into chunks of C (merge_chunk); the leader of a chunk
+// folds its pieces, for every row of the segment's unit, in position order.
+//   * Chunk 0 is led by wave g of this kernel, g the segment's index.  With
+//     one chunk (n small, the usual case) it writes the output rows: two
+//     dependent memory round trips, the segment's owners then its partials.
+//   * A segment far longer than the rest (one long context among short
+//     ones) has several chunks, and chunk c >= 1 is led by this kernel's
+//     wave u0 + c * C.  The main kernel's wave of that index has a range
+//     starting inside the segment (its predecessor owns part of it too), and
+//     it recorded that segment, so the leader finds it in one load.  Each
+//     leader writes its chunk's max, sum and output over the
+//     partial row of the chunk's first piece (no other wave reads that row),
+//     then counts itself in on the segment's counter, reset to 0 by the main
+//     kernel.  The leader that arrives last folds the chunks in chunk order
+//     and writes the output rows, so the order depends on positions only.
+//     The release and acquire around the counter write back and invalidate
+//     an XCD's L2, which is why segments with many pieces as the rule (few,
+//     long sequences) go to decode_merge instead.
+// Wave g also writes the zero rows of segment g when its sequence is empty.
+// Lanes are (four-float chunk ch, row group rg); row group rg owns rows
+// hh = rg + RGN * r, r < RG, of the unit (one row with the VALU body).
+// Grid: max(segments, main-kernel waves).
+
+// Pieces per chunk of a segment of n pieces: one chunk up to two rounds of
+// KB loads, else about sqrt(n), so that the leaders' folds and the last
+// fold over the chunks take about as many rounds.
+template <int KB>
+__device__ __forceinline__ int merge_chunk(int n) {
+  if (n <= 2 * KB) return n;
+  const int c = (int)ceilf(sqrtf((float)n));
+  return c > 2 * KB ? c : 2 * KB;
+}
+
 template <int D, typename OUT, int RG>
-__global__ __launch_bounds__(64) void decode_merge_units(Params p) {
+__global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
   constexpr int CH = D / 4;      // 4-float chunks per row
   constexpr int RGN = 64 / CH;   // row groups per wave
-  constexpr int KB = 2;          // pieces per row whose loads are issued together
+  constexpr int KB = RG <= 4 ? 4 : 2;   // pieces per row whose loads are issued together
   const int lane = lane_id();
   const int ch = lane % CH, rg = lane / CH;
-  const int64_t g = (int64_t)blockIdx.x;   // seq * units + unit
-  const int unit = (int)(g % p.units);
-  const int seq = (int)(g / p.units);
-  const int h0 = (unit % p.head_tiles) * 16;   // the unit's first head within its group
-  const int nh = min(p.gu, p.group - h0);      // rows the unit holds
-  OUT *out = static_cast<OUT *>(p.out) +
-             ((int64_t)seq * p.num_q_heads + (unit / p.head_tiles) * p.group + h0) * D + 4 * ch;
-  const int L = seq_len(p, seq);
-  if (L == 0) {
+  const int b = (int)blockIdx.x;
+  const int64_t segs = (int64_t)p.num_seqs * p.units;
+  const int ux = p.units / p.xsplit;
+
+  float mg[RG], sg[RG];
+  f32x4 ag[RG];
+  // Fold `count` partial rows, ids first, first + step, ... (in that order),
+  // for every row this lane group owns, into (mg, sg, ag).
+  auto fold = [&](int64_t first, int count, int step, int nh) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      mg[r] = -INFINITY;
+      sg[r] = 0.f;
+      ag[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i0 = 0; i0 < count; i0 += KB) {
+      float pm[KB][RG], ps[KB][RG];
+      f32x4 po[KB][RG];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const int hh = rg + RGN * r;
+          pm[k][r] = -INFINITY;
+          ps[k][r] = 0.f;
+          po[k][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (i0 + k < count && hh < nh) {
+            const int64_t row = (first + (int64_t)(i0 + k) * step) * p.gu + hh;
+            pm[k][r] = p.ws_max[row];
+            ps[k][r] = p.ws_sum[row];
+            po[k][r] = *reinterpret_cast<const f32x4 *>(p.ws_acc + row * D + 4 * ch);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        if (i0 + k < count) {
+#pragma unroll
+          for (int r = 0; r < RG; ++r) {
+            const float mn = fmaxf(mg[r], pm[k][r]);
+            const float a = fast_exp2(mg[r] - mn), c = fast_exp2(pm[k][r] - mn);
+            ag[r] = ag[r] * a + po[k][r] * c;
+            sg[r] = sg[r] * a + ps[k][r] * c;
+            mg[r] = mn;
+          }
+        }
+      }
+    }
+  };
+  // Segment g's first output row (query head), rows, output pointer.
+  auto rows_of = [&](int64_t g, int &nh) -> OUT * {
+    const int unit = (int)(g % p.units);
+    int qh0;
+    if (p.gu == 1) {   // VALU body: one query head per unit
+      qh0 = unit;
+      nh = 1;
+    } else {
+      const int h0 = (unit % p.head_tiles) * 16;
+      qh0 = (unit / p.head_tiles) * p.group + h0;
+      nh = min(p.gu, p.group - h0);
+    }
+    return static_cast<OUT *>(p.out) + ((g / p.units) * p.num_q_heads + qh0) * D + 4 * ch;
+  };
+  auto store_rows = [&](OUT *out, int nh, bool zero) {
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int hh = rg + RGN * r;
-      if (hh < nh) store_out4<OUT>(out + (int64_t)hh * D, 0.f, 0.f, 0.f, 0.f);
+      if (hh < nh) {
+        const float inv = zero ? 0.f : 1.f / sg[r];
+        store_out4<OUT>(out + (int64_t)hh * D, ag[r][0] * inv, ag[r][1] * inv, ag[r][2] * inv,
+                        ag[r][3] * inv);
+      }
     }
-    return;
-  }
-  if (own_tiles(p, L) == 0) return;
-  const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
-  const int n = u1 - u0 + 1;
-  if (n <= 1) return;   // one piece: the main kernel wrote the rows
-  const int x = unit % p.xsplit, ux = p.units / p.xsplit;
-  const int64_t id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
-  float mg[RG], sg[RG];
-  f32x4 ag[RG];
+  };
+  // Lead chunk c of segment g (owners u0..u1).
+  auto lead = [&](int64_t g, int u0, int u1, int c) {
+    const int n = u1 - u0 + 1;
+    const int C = merge_chunk<KB>(n), nc = (n + C - 1) / C;
+    const int unit = (int)(g % p.units), seq = (int)(g / p.units);
+    const int64_t id0 = (int64_t)(unit % p.xsplit) * p.id_stride + (int64_t)seq * ux +
+                        unit / p.xsplit + u0;
+    const int64_t first = id0 + (int64_t)c * C;
+    int nh;
+    OUT *out = rows_of(g, nh);
+    fold(first, min(C, n - c * C), 1, nh);
+    if (nc == 1) {
+      store_rows(out, nh, false);
+      return;
+    }
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    mg[r] = -INFINITY;
-    sg[r] = 0.f;
-    ag[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int i0 = 0; i0 < n; i0 += KB) {
-    float pm[KB][RG], ps[KB][RG];
-    f32x4 po[KB][RG];
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const int hh = rg + RGN * r;
-        pm[j][r] = -INFINITY;
-        ps[j][r] = 0.f;
-        po[j][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (i0 + j < n && hh < nh) {
-          const int64_t row = (id0 + i0 + j) * p.gu + hh;
-          pm[j][r] = p.ws_max[row];
-          ps[j][r] = p.ws_sum[row];
-          po[j][r] = *reinterpret_cast<const f32x4 *>(p.ws_acc + row * D + 4 * ch);
+    for (int r = 0; r < RG; ++r) {
+      const int hh = rg + RGN * r;
+      if (hh < nh) {
+        const int64_t row = first * p.gu + hh;
+        *reinterpret_cast<f32x4 *>(p.ws_acc + row * D + 4 * ch) = ag[r];
+        if (ch == 0) {
+          p.ws_max[row] = mg[r];
+          p.ws_sum[row] = sg[r];
         }
       }
     }
+    // Release this chunk's rows to the other XCDs, then count in; the last
+    // leader acquires the others' rows before reading them.
+    __threadfence();
+    int before = 0;
+    if (lane == 0) before = atomicAdd(p.seg_cnt + g, 1);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != nc - 1) return;
+    __threadfence();
+    fold(id0, nc, C, nh);
+    store_rows(out, nh, false);
+  };
+
+  // Chunk 0 of segment b, or its zero rows.
+  if (b < segs) {
+    if (seq_len(p, (int)(b / p.units)) == 0) {
+      int nh;
+      OUT *out = rows_of(b, nh);
 #pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      if (i0 + j < n) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          const float mn = fmaxf(mg[r], pm[j][r]);
-          const float a = fast_exp2(mg[r] - mn), b = fast_exp2(pm[j][r] - mn);
-          ag[r] = ag[r] * a + po[j][r] * b;
-          sg[r] = sg[r] * a + ps[j][r] * b;
-          mg[r] = mn;
-        }
-      }
+      for (int r = 0; r < RG; ++r) ag[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      store_rows(out, nh, true);
+    } else {
+      const int u0 = p.seg_units[2 * (int64_t)b], u1 = p.seg_units[2 * (int64_t)b + 1];
+      if (u1 > u0) lead(b, u0, u1, 0);   // one piece: the main kernel wrote the rows
     }
   }
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int hh = rg + RGN * r;
-    if (hh < nh) {
-      const float inv = 1.f / sg[r];
-      store_out4<OUT>(out + (int64_t)hh * D, ag[r][0] * inv, ag[r][1] * inv, ag[r][2] * inv,
-                      ag[r][3] * inv);
+  // A chunk c >= 1 this wave leads: in the segment the main kernel's wave b
+  // started in.
+  if (b < p.waves) {
+    const int j = b / p.xsplit;
+    const int g = p.wave_segs[b];
+    if (g >= 0) {
+      const int u0 = p.seg_units[2 * (int64_t)g], u1 = p.seg_units[2 * (int64_t)g + 1];
+      const int n = u1 - u0 + 1;
+      if (n > 2 * KB && j > u0 && j <= u1) {   // several chunks, not chunk 0
+        const int C = merge_chunk<KB>(n);
+        if ((j - u0) % C == 0) lead(g, u0, u1, (j - u0) / C);
+      }
     }
   }
 }
@@ -1591,10 +1709,12 @@ hipError_t plan_prefix(const DecodeArgs &a, Params &p) {
   return hipSuccess;
 }
 
-// Expected pieces per segment up to which a balanced split's MFMA units are
-// merged one wave per segment (decode_merge_units folds a row's pieces two
-// loads at a time, so more pieces mean more dependent rounds).
-constexpr int64_t kUnitMergeMaxPieces = 4;
+// Expected pieces per segment up to which a balanced split (no shared
+// prefix) is merged one wave per segment (decode_merge_segments).  Beyond
+// it most segments span many pieces, and decode_merge's multi-wave rows,
+// combined through LDS, avoid the cross-XCD synchronisation that the
+// segment merge needs for such segments.
+constexpr int64_t kSegmentMergeMaxPieces = 4;
 
 // Waves per output row for the merge: enough that each wave's piece groups
 // get at most one batch of loads for the pieces a row is expected to have
@@ -1626,18 +1746,20 @@ hipError_t launch_merge_d(const Params &p, int64_t rows, int nw, hipStream_t st)
 }
 
 template <int D, typename OUT>
-hipError_t launch_merge_units_d(const Params &p, int64_t segs, hipStream_t st) {
+hipError_t launch_merge_segments_d(const Params &p, int64_t segs, hipStream_t st) {
   constexpr int RGN = 64 / (D / 4);
   const int rg = (p.gu + RGN - 1) / RGN;
-  const dim3 grid((unsigned)segs);
+  const int64_t n = segs > p.waves ? segs : p.waves;
+  if (n > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n);
   if (rg <= 1)
-    hipLaunchKernelGGL((decode_merge_units<D, OUT, 1>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 1>), grid, dim3(64), 0, st, p);
   else if (rg <= 2)
-    hipLaunchKernelGGL((decode_merge_units<D, OUT, 2>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 2>), grid, dim3(64), 0, st, p);
   else if (rg <= 4)
-    hipLaunchKernelGGL((decode_merge_units<D, OUT, 4>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 4>), grid, dim3(64), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_merge_units<D, OUT, 8>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 8>), grid, dim3(64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1645,15 +1767,17 @@ template <typename OUT>
 hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
   const int64_t rows = (int64_t)a.num_seqs * p.units * p.gu;
   if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
-  // Balanced split of MFMA units (several rows per segment) with few pieces
-  // per segment: one wave per segment.
-  if (a.partition_size < 0 && a.prefix_len == 0 && p.gu > 1) {
+  // Balanced split without a shared prefix, segments expected to span few
+  // pieces (many sequences): one wave per segment.
+  if (a.partition_size < 0 && a.prefix_len == 0) {
+    if (p.waves <= 0 || p.wave_segs == nullptr || p.seg_cnt == nullptr)
+      return hipErrorInvalidValue;
     const int64_t segs = (int64_t)a.num_seqs * p.units;
     const int64_t sx = (int64_t)a.num_seqs * (p.units / p.xsplit);
     const int64_t est = sx > 0 ? (p.waves / p.xsplit + sx - 1) / sx + 1 : 1;
-    if (est <= kUnitMergeMaxPieces) {
-      if (a.head_dim == 64) return launch_merge_units_d<64, OUT>(p, segs, st);
-      return launch_merge_units_d<128, OUT>(p, segs, st);
+    if (est <= kSegmentMergeMaxPieces) {
+      if (a.head_dim == 64) return launch_merge_segments_d<64, OUT>(p, segs, st);
+      return launch_merge_segments_d<128, OUT>(p, segs, st);
     }
   }
   if (a.head_dim == 64) return launch_merge_d<64, OUT>(p, rows, merge_waves<64>(a, p), st);
@@ -1714,6 +1838,10 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.ws_sum = a.ws_sum;
   p.ws_acc = a.ws_acc;
   p.seg_units = a.seg_units;
+  // Records for the waves' merge (balanced split without a shared prefix).
+  const bool wave_merge = a.partition_size < 0 && a.prefix_len == 0;
+  p.seg_cnt = wave_merge ? a.seg_cnt : nullptr;
+  p.wave_segs = wave_merge ? a.wave_segs : nullptr;
   p.num_blocks = a.num_blocks;
   p.num_seqs = a.num_seqs;
   p.num_q_heads = a.num_q_heads;

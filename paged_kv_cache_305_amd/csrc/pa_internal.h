@@ -31,6 +31,8 @@ struct DecodeArgs {
   uint32_t flags;           // PA_DECODE_* bits
   float *ws_max, *ws_sum, *ws_acc;  // split partials, null when every row is written whole
   int32_t *seg_units;               // balanced mode: 2 ints per (sequence, head unit)
+  int32_t *seg_cnt;                 // balanced mode: 1 int per (sequence, head unit)
+  int32_t *wave_segs;               // balanced mode: 1 int per wave
   int32_t prefix_len;               // shared prefix tokens (0: none)
   float *pf_max, *pf_sum, *pf_acc;  // shared-prefix partials
   int32_t xcd_weights[8];           // balanced mode: relative tile share per XCD
@@ -80,10 +82,13 @@ void balance_weights(int32_t out[8]);
 // partial rows, each a base-2 max, a sum and head_dim unnormalised outputs,
 // then `segments` pairs of int32 (balanced mode's first/last owning wave).
 struct WorkspaceLayout {
-  size_t rows, max_off, sum_off, acc_off, seg_off, pf_max_off, pf_sum_off, pf_acc_off, total;
+  size_t rows, max_off, sum_off, acc_off, seg_off, cnt_off, wave_off, pf_max_off, pf_sum_off,
+      pf_acc_off, total;
 };
+// segments: balanced split's (sequence, head unit) pairs (2 + 1 ints each);
+// waves: its most waves (1 int each).
 WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments,
-                                 size_t prefix_rows = 0);
+                                 size_t waves, size_t prefix_rows = 0);
 
 // Kernel launchers (pa_decode.hip, pa_cache.hip); they return hipError_t as int.
 int launch_decode(const DecodeArgs &a, void *stream);

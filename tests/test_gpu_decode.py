@@ -92,6 +92,26 @@ def test_many_short_sequences_merged_per_segment(gpu, kw):
         _check(gpu, case, BAL, out_dtype=od)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(),                                              # G 8: 8 rows per segment
+    dict(num_q_heads=8, num_kv_heads=8),                 # VALU body: one row per segment
+    dict(num_q_heads=16, num_kv_heads=1),                # G 16: 8 rows per row group
+    dict(num_q_heads=32, num_kv_heads=8, head_dim=64),   # G 4, d 64
+])
+def test_one_long_context_among_many_short_ones(gpu, kw):
+    """Many short sequences make the host merge one wave per segment, while
+    the long sequence's segments span 160 to 1300 pieces each: their chunks
+    are merged by several waves and combined by the last one to finish."""
+    rng = np.random.default_rng(7)
+    lens = tuple(int(x) for x in rng.integers(0, 65, size=599)) + (40000,)
+    case = W.make_case("70b", device="cuda", batch=600, lens=lens, **kw)
+    idx = sorted(set(int(i) for i in rng.choice(599, 40, replace=False)) | {599})
+    for od in (torch.float32, torch.bfloat16):
+        out, _ = _check(gpu, case, BAL, out_dtype=od, idx=idx)
+        # Whichever chunk leader finishes last, the chunks are folded in order.
+        assert torch.equal(out, gpu_decode(gpu, case, partition_size=BAL, out_dtype=od))
+
+
 @pytest.mark.parametrize("name,kw", [("7b", dict(batch=3, len_range=(1, 300))),
                                      ("70b", dict(batch=3, len_range=(1, 300))),
                                      ("tiny", {})])
