@@ -111,7 +111,9 @@ int32_t pa_version(void);
  *  flags          PA_DECODE_* bits (0: K/V streamed, each block read once).
  *  workspace      device scratch of at least
  *                 pa_paged_attention_workspace_bytes(...) bytes when that is
- *                 nonzero (caller-owned, contents need not be initialised).
+ *                 nonzero (caller-owned, contents need not be initialised;
+ *                 the call's kernels reset what they count with).  Calls
+ *                 that may overlap (other streams) need workspaces of their own.
  *  Supported: head_dim in {64, 128}, block_size in {16, 32, 64},
  *  kv_dtype/out_dtype in {PA_FP32, PA_BF16}; anything else returns
  *  PA_ERR_UNSUPPORTED.  bf16 outputs are rounded to nearest even.
