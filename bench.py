@@ -44,13 +44,15 @@ WORKLOADS = {
               "32/8 heads, d 128, bf16, Bs 16, CoW step",
     "long": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 16",
     "long32": "long-context split-K: batch 8, L=32768, 32/8 heads, d 128, bf16, Bs 32",
+    "mixed": "70B-shaped GQA decode with one long context: batch 256, 64/8 heads, d 128, bf16, "
+             "Bs 16, 255 x L~U[128,4096] + one L=131072",
     "swap": "preemption swap of the 7B-shaped step's blocks: GPU pool <-> pinned host pool "
             "(swap_blocks), both directions",
 }
 HOST_LINK_PEAK_GBS = 64.0   # PCIe Gen5 x16, one direction
 
 
-MODEL_LAYERS = {"7b": 32, "70b": 80}
+MODEL_LAYERS = {"7b": 32, "70b": 80, "mixed": 80}
 
 
 def log(msg):
@@ -121,7 +123,8 @@ def block_waste(step, lens):
 # Longest context each workload reserves when storage is one contiguous
 # max-length region per sequence (the prior allocation scheme the pages
 # compare against): the upper end of its length distribution.
-MAX_CONTEXT = {"7b": 2048, "70b": 4096, "long": 32768, "shared": 4000 + 512 + 1}
+MAX_CONTEXT = {"7b": 2048, "70b": 4096, "long": 32768, "shared": 4000 + 512 + 1,
+               "mixed": 131072}
 
 
 def waste_report(block_sizes=(8, 16, 32, 64)):
@@ -449,7 +452,7 @@ def main():
                 # stands (its own block size, batch and placement, default
                 # cache write and prefix use): any other variant gets none.
                 traffic=counter_traffic(args.workload, args.partition_size)
-                if args.block_size in (None, W.CONFIGS[args.workload]["block_size"]) and args.batch is None
+                if args.block_size in (None, W.CONFIGS.get(args.workload, {}).get("block_size")) and args.batch is None
                 and args.table_order == "random" and args.cache_write == "auto"
                 and not args.no_prefix else None,
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),

@@ -1452,14 +1452,15 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
 // hh = rg + RGN * r, r < RG, of the unit (one row with the VALU body).
 // Grid: max(segments, main-kernel waves).
 
-// Pieces per chunk of a segment of n pieces: one chunk up to two rounds of
-// KB loads, else about sqrt(n), so that the leaders' folds and the last
-// fold over the chunks take about as many rounds.
+// Pieces per chunk of a segment of n pieces: one chunk up to four rounds of
+// KB loads (no synchronisation), else max(4 KB, about sqrt(n)), so that the
+// leaders' folds and the last fold over the chunks take about as many
+// rounds.
 template <int KB>
 __device__ __forceinline__ int merge_chunk(int n) {
-  if (n <= 2 * KB) return n;
+  if (n <= 4 * KB) return n;
   const int c = (int)ceilf(sqrtf((float)n));
-  return c > 2 * KB ? c : 2 * KB;
+  return c > 4 * KB ? c : 4 * KB;
 }
 
 template <int D, typename OUT, int RG>
@@ -1571,13 +1572,14 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
       }
     }
     // Release this chunk's rows to the other XCDs, then count in; the last
-    // leader acquires the others' rows before reading them.
-    __threadfence();
+    // leader acquires the others' rows before reading them.  (Release and
+    // acquire apart: each costs an XCD-wide L2 write-back or invalidate.)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     int before = 0;
     if (lane == 0) before = atomicAdd(p.seg_cnt + g, 1);
     before = __builtin_amdgcn_readfirstlane(before);
     if (before != nc - 1) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     fold(id0, nc, C, nh);
     store_rows(out, nh, false);
   };
@@ -1603,7 +1605,7 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
     if (g >= 0) {
       const int u0 = p.seg_units[2 * (int64_t)g], u1 = p.seg_units[2 * (int64_t)g + 1];
       const int n = u1 - u0 + 1;
-      if (n > 2 * KB && j > u0 && j <= u1) {   // several chunks, not chunk 0
+      if (n > 4 * KB && j > u0 && j <= u1) {   // several chunks, not chunk 0
         const int C = merge_chunk<KB>(n);
         if ((j - u0) % C == 0) lead(g, u0, u1, (j - u0) / C);
       }

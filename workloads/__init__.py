@@ -32,6 +32,8 @@ import numpy as np
 import torch
 
 CONFIG_ORDER = ("tiny", "7b", "70b", "shared", "long")
+# Workloads beyond the five, seeded after them in this order.
+EXTRA_ORDER = ("mixed",)
 
 # Workload shapes.  "lens" fixes the lengths; "len_range" draws them
 # uniformly (inclusive).  pool: "1.5x" = ceil(1.5 * blocks needed),
@@ -59,12 +61,19 @@ CONFIGS = {
     "long": dict(batch=8, lens=(32768,) * 8, num_q_heads=32, num_kv_heads=8,
                  head_dim=128, block_size=16, dtype="bf16", pool="exact",
                  partition_size=512),
+    # The 70B shape with one long context in the batch (continuous batching
+    # of one long request among short ones): 255 contexts U[128, 4096] and
+    # one of 131072 at a seeded position.
+    "mixed": dict(batch=256, len_range=(128, 4096), long_len=131072, num_q_heads=64,
+                  num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", pool="exact"),
 }
 
 TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
 
 def seed_for(name: str) -> int:
+    if name in EXTRA_ORDER:
+        return 305 + len(CONFIG_ORDER) + EXTRA_ORDER.index(name)
     return 305 + CONFIG_ORDER.index(name)
 
 
@@ -177,6 +186,8 @@ def case_structure(name: str, *, batch: Optional[int] = None, seed: Optional[int
         lo, hi = len_range or cfg["len_range"]
         b = batch or cfg["batch"]
         lengths = rng.integers(lo, hi + 1, size=b).astype(np.int64)
+        if "long_len" in cfg:   # one long context at a seeded position
+            lengths[int(rng.integers(b))] = cfg["long_len"]
     else:
         lengths = np.asarray(cfg["lens"], dtype=np.int64)
         if batch is not None:   # the fixed lengths, cycled or cut to the batch
