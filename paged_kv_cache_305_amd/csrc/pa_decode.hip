@@ -1314,6 +1314,14 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
   OUT *out = static_cast<OUT *>(p.out) + ((int64_t)seq * p.num_q_heads + qh) * D;
   const int L = seq_len(p, seq);
   const bool balanced = p.partition_size < 0;
+  // Balanced split: the segment's owning waves, requested together with the
+  // length (they are stale, and unused, when the sequence has no own tiles).
+  const int64_t g = (int64_t)seq * p.units + unit;
+  int u0 = 0, u1 = 0;
+  if (balanced) {
+    u0 = p.seg_units[2 * g];
+    u1 = p.seg_units[2 * g + 1];
+  }
   if (L == 0) {
     if (balanced && w == 0 && pg == 0) store_out4<OUT>(out + 4 * ch, 0.f, 0.f, 0.f, 0.f);
     return;
@@ -1322,8 +1330,6 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
   int n = 0;
   if (balanced) {
     if (own_tiles(p, L) > 0) {
-      const int64_t g = (int64_t)seq * p.units + unit;
-      const int u0 = p.seg_units[2 * g], u1 = p.seg_units[2 * g + 1];   // owning waves
       const int x = unit % p.xsplit, ux = p.units / p.xsplit;
       n = u1 - u0 + 1;
       id0 = (int64_t)x * p.id_stride + (int64_t)seq * ux + unit / p.xsplit + u0;
@@ -1586,15 +1592,18 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
 
   // Chunk 0 of segment b, or its zero rows.
   if (b < segs) {
-    if (seq_len(p, (int)(b / p.units)) == 0) {
+    // The owning waves are requested with the length (stale, and unused,
+    // when the sequence is empty).
+    const int L = seq_len(p, (int)(b / p.units));
+    const int u0 = p.seg_units[2 * (int64_t)b], u1 = p.seg_units[2 * (int64_t)b + 1];
+    if (L == 0) {
       int nh;
       OUT *out = rows_of(b, nh);
 #pragma unroll
       for (int r = 0; r < RG; ++r) ag[r] = f32x4{0.f, 0.f, 0.f, 0.f};
       store_rows(out, nh, true);
-    } else {
-      const int u0 = p.seg_units[2 * (int64_t)b], u1 = p.seg_units[2 * (int64_t)b + 1];
-      if (u1 > u0) lead(b, u0, u1, 0);   // one piece: the main kernel wrote the rows
+    } else if (u1 > u0) {   // one piece: the main kernel wrote the rows
+      lead(b, u0, u1, 0);
     }
   }
   // A chunk c >= 1 this wave leads: in the segment the main kernel's wave b
