@@ -339,6 +339,10 @@ def main():
     ap.add_argument("--cache-write", choices=["auto", "fused", "separate"], default="auto",
                     help="write the new tokens inside the attention launch (fused), with "
                          "reshape_and_cache before it (separate); auto = fused")
+    ap.add_argument("--cow", choices=["auto", "fused", "separate"], default="auto",
+                    help="copy-on-write pairs: inside the attention launch with the new tokens "
+                         "(fused, when each pair is a new-token block) or with copy_blocks "
+                         "first (separate); auto = fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--block-size", type=int, default=None,
@@ -388,11 +392,16 @@ def main():
                                   block_size=args.block_size, table_order=args.table_order,
                                   prefix=not args.no_prefix, batch=args.batch)
     step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
+    step.cow_fused = {"auto": None, "fused": True, "separate": False}[args.cow]
     torch.cuda.synchronize()
     kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
     if step.uses_fused_write:   # the launch also reads and stores each new token's K and V
         attn_bytes += 2 * step.new_key.numel() * step.new_key.element_size() * 2 + \
             step.slot_mapping.numel() * 8
+    if step.uses_fused_copy:    # ... and copies each pair's block, K and V (read + write)
+        block_bytes = step.num_kv_heads * step.block_size * step.head_dim * \
+            step.query.element_size()
+        attn_bytes += step.num_pairs * 2 * block_bytes * 2 + step.cow_src.numel() * 8
     flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=device)
     K, W_ = args.steps, args.warmup
     def ev():
@@ -454,7 +463,7 @@ def main():
                 traffic=counter_traffic(args.workload, args.partition_size)
                 if args.block_size in (None, W.CONFIGS.get(args.workload, {}).get("block_size")) and args.batch is None
                 and args.table_order == "random" and args.cache_write == "auto"
-                and not args.no_prefix else None,
+                and args.cow == "auto" and not args.no_prefix else None,
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
                 kernel_source_digest=kernel_source_digest())
     result = {
@@ -478,6 +487,9 @@ def main():
                    "shared_prefix_tokens": step.prefix_len,
                    "cache_write": "inside the attention launch" if step.uses_fused_write
                                   else "reshape_and_cache before the attention",
+                   "copy_on_write": "none" if not step.num_pairs else
+                                    "inside the attention launch" if step.uses_fused_copy
+                                    else "copy_blocks before the attention",
                    "flush_between_steps": flush is not None, **info,
                    **block_waste(step, lens)},
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

@@ -150,13 +150,27 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
  *                 copies a shared block first).  PA_VALIDATE=1 checks the
  *                 position; a slot outside the pool is skipped like a
  *                 negative one.
+ *  cow_src        NULL, or int64 [num_seqs] (device): copy-on-write inside
+ *                 the launch (note-023, Concepts; inferensys glossary,
+ *                 second paragraph: a shared block is copied when a sharer
+ *                 writes).  cow_src[i] >= 0 is the block whose whole
+ *                 contents (K and V, all heads and slots) sequence i's new
+ *                 token block, slot_mapping[i] / block_size, takes before
+ *                 the token is written: the pair (cow_src[i], that block)
+ *                 that pa_seq_append_slot returned, which pa_copy_blocks
+ *                 would otherwise copy first.  Sequence i's attention reads
+ *                 the source in that block's place.  Another sequence of
+ *                 the call may write its new token into a source block in
+ *                 place only at the same offset (true of sharers of a partly
+ *                 filled block, which have equal lengths).  Negative: no
+ *                 copy.  PA_VALIDATE=1 checks each source and offset.
  *  Every other argument as in pa_paged_attention_decode (key_cache and
  *  value_cache are written here).
  * ---------------------------------------------------------------------- */
 pa_status pa_paged_attention_decode_append(
     void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
-    const void *new_value, const int64_t *slot_mapping, const int32_t *block_tables,
-    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    const void *new_value, const int64_t *slot_mapping, const int64_t *cow_src,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
     int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
     pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
@@ -174,9 +188,10 @@ pa_status pa_paged_attention_decode_append(
  *  prefix_len     positive multiple of block_size, <= every context_lens[i];
  *                 block_tables rows agree on their first prefix_len /
  *                 block_size entries (PA_VALIDATE=1 checks both).
- *  new_key, new_value, slot_mapping
- *                 all NULL, or the step's new tokens exactly as in
- *                 pa_paged_attention_decode_append (written by this call).
+ *  new_key, new_value, slot_mapping, cow_src
+ *                 new tokens all NULL, or the step's new tokens and copies
+ *                 exactly as in pa_paged_attention_decode_append (written
+ *                 by this call).
  *                 A new token sits after the prefix (context_lens[i] >
  *                 prefix_len where slot_mapping[i] >= 0): its block is the
  *                 sequence's own.  PA_VALIDATE=1 checks this too.
@@ -187,7 +202,7 @@ pa_status pa_paged_attention_decode_append(
 pa_status pa_paged_attention_decode_prefix(void *out, const void *query, void *key_cache,
                                            void *value_cache, const void *new_key,
                                            const void *new_value, const int64_t *slot_mapping,
-                                           const int32_t *block_tables,
+                                           const int64_t *cow_src, const int32_t *block_tables,
                                            const int32_t *context_lens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,

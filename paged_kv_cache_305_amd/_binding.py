@@ -65,11 +65,11 @@ def _declare(lib):
         "pa_paged_attention_decode": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                             i64, i32, f32, i32, i32, i32, ctypes.c_uint32, vp, sz,
                                             vp]),
-        "pa_paged_attention_decode_append": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+        "pa_paged_attention_decode_append": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
-        "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+        "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_prefix_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
@@ -246,10 +246,14 @@ def paged_attention_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, 
         _dtype_code_of(kv_dtype)))
 
 
-def _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, dtype, dev):
-    """Device pointers of a step's new tokens (all three given) or zeros (none)."""
+def _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, dtype, dev,
+                    cow_src=None):
+    """Device pointers of a step's new tokens (all three given) and of the
+    optional in-launch copy-on-write sources, or zeros (none)."""
     if new_key is None and new_value is None and slot_mapping is None:
-        return 0, 0, 0
+        if cow_src is not None:
+            raise ValueError("cow_src needs the new tokens")
+        return 0, 0, 0, 0
     if new_key is None or new_value is None or slot_mapping is None:
         raise ValueError("new_key, new_value and slot_mapping go together")
     for t, n in ((new_key, "new_key"), (new_value, "new_value"), (slot_mapping, "slot_mapping")):
@@ -260,7 +264,13 @@ def _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, dtype,
         raise TypeError("new_key and new_value must have the pools' dtype")
     if slot_mapping.dtype != _torch().int64 or slot_mapping.shape != (B,):
         raise ValueError("slot_mapping must be int64 [num_seqs]")
-    return new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr()
+    cow = 0
+    if cow_src is not None:
+        _dev(cow_src, "cow_src", dev)
+        if cow_src.dtype != _torch().int64 or cow_src.shape != (B,):
+            raise ValueError("cow_src must be int64 [num_seqs]")
+        cow = cow_src.data_ptr()
+    return new_key.data_ptr(), new_value.data_ptr(), slot_mapping.data_ptr(), cow
 
 
 def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tables,
@@ -268,11 +278,11 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
                                   block_size: int, max_context_len: int, scale: float,
                                   workspace=None, num_blocks: Optional[int] = None,
                                   new_key=None, new_value=None, slot_mapping=None,
-                                  stream=None):
+                                  cow_src=None, stream=None):
     """Decode attention when every sequence's first prefix_len tokens are the
     same physical blocks (sequence 0's): those are read once for all rows.
-    new_key, new_value and slot_mapping as in paged_attention_decode (each
-    new token after the prefix)."""
+    new_key, new_value, slot_mapping and cow_src as in paged_attention_decode
+    (each new token after the prefix)."""
     lib = load()
     dev = query.device
     for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
@@ -286,7 +296,8 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
     if tuple(out.shape) != (B, hq, d):
         raise ValueError("out must have the query's shape")
     nb = int(key_cache.shape[0]) if num_blocks is None else int(num_blocks)
-    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev)
+    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev,
+                           cow_src)
     need = paged_attention_prefix_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
                                                   prefix_len, query.dtype)
     if workspace is None:
@@ -304,7 +315,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                            num_kv_heads: int, block_size: int, max_context_len: int,
                            scale: float, partition_size: int = 0, workspace=None,
                            num_blocks: Optional[int] = None, kv_reused: bool = False,
-                           new_key=None, new_value=None, slot_mapping=None, stream=None):
+                           new_key=None, new_value=None, slot_mapping=None, cow_src=None,
+                           stream=None):
     """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables.
 
     kv_reused: some physical blocks are read by several sequences (shared
@@ -312,10 +324,14 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
 
     new_key, new_value ([B, Hkv, d]) and slot_mapping (int64 [B]), given
     together: each sequence's last position is this new token, written into
-    its slot by the same launch (pa_paged_attention_decode_append)."""
+    its slot by the same launch (pa_paged_attention_decode_append).
+    cow_src (int64 [B], optional with them): the copy-on-write source of
+    each sequence's new-token block, copied inside the launch (-1: none)."""
     lib = load()
     dev = query.device
     appending = new_key is not None or new_value is not None or slot_mapping is not None
+    if cow_src is not None and not appending:
+        raise ValueError("cow_src needs the new tokens")
     for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
                  (value_cache, "value_cache"), (block_tables, "block_tables"),
                  (context_lens, "context_lens")):
@@ -336,7 +352,8 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     chunk = num_kv_heads * d * block_size
     if key_cache.numel() < nb * chunk or value_cache.numel() < nb * chunk:
         raise ValueError("pools hold fewer than num_blocks blocks")
-    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev)
+    news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev,
+                           cow_src)
     need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
                                            partition_size, query.dtype)
     if need and workspace is None:

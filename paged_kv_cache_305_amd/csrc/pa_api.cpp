@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -189,7 +190,8 @@ namespace {
 // pa_paged_attention_decode_append.
 pa_status decode_call(const char *fn, void *out, const void *query, const void *key_cache,
                       const void *value_cache, const void *new_key, const void *new_value,
-                      const int64_t *slot_mapping, const int32_t *block_tables,
+                      const int64_t *slot_mapping, const int64_t *cow_src,
+                      const int32_t *block_tables,
                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
@@ -241,6 +243,8 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                      "needed", fn);
     if (!aligned16(new_key) || !aligned16(new_value))
       return pa_fail(PA_ERR_INVALID_ARG, "%s: new_key and new_value must be 16-byte aligned", fn);
+  } else if (cow_src) {
+    return pa_fail(PA_ERR_INVALID_ARG, "%s: cow_src needs the new tokens (slot_mapping)", fn);
   }
 
   const int32_t parts = partitions_for(max_context_len, partition_size);
@@ -312,6 +316,28 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
           return pa_fail(PA_ERR_INVALID_ARG, "%s: sequence %d appends at position %d, inside "
                          "the shared prefix", fn, i, pos);
       }
+      if (cow_src) {
+        // A copy source is a block other than the slot's, and a sequence
+        // that writes a new token into a copy source in place writes it at
+        // the same offset as the sequence copying it (they shared the
+        // partly filled block, so they had the same length).
+        std::vector<int64_t> src;
+        s = to_host(src, cow_src, (size_t)num_seqs, stream);
+        if (s != PA_OK) return s;
+        std::unordered_map<int64_t, int64_t> slot_of_block;   // block -> slot written in it
+        for (int32_t i = 0; i < num_seqs; ++i)
+          if (slots[i] >= 0) slot_of_block[slots[i] / block_size] = slots[i];
+        for (int32_t i = 0; i < num_seqs; ++i) {
+          if (src[i] < 0) continue;
+          if (slots[i] < 0 || src[i] >= num_blocks || src[i] == slots[i] / block_size)
+            return pa_fail(PA_ERR_INVALID_ARG, "%s: cow_src[%d] = %lld needs a new token and "
+                           "must be another block of the pool", fn, i, (long long)src[i]);
+          const auto w = slot_of_block.find(src[i]);
+          if (w != slot_of_block.end() && w->second % block_size != slots[i] % block_size)
+            return pa_fail(PA_ERR_INVALID_ARG, "%s: cow_src[%d] = %lld is written at another "
+                           "offset by this call", fn, i, (long long)src[i]);
+        }
+      }
     }
   }
 
@@ -325,6 +351,7 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
   a.new_key = new_key;
   a.new_value = new_value;
   a.slots = slot_mapping;
+  a.cow_src = cow_src;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -373,7 +400,7 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
                                     void *stream) {
   pa_clear_error();
   return decode_call("pa_paged_attention_decode", out, query, key_cache, value_cache, nullptr,
-                     nullptr, nullptr, block_tables, context_lens, num_seqs, num_q_heads,
+                     nullptr, nullptr, nullptr, block_tables, context_lens, num_seqs, num_q_heads,
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
                      max_context_len, scale, partition_size, kv_dtype, out_dtype, flags,
                      workspace, workspace_bytes, stream);
@@ -382,7 +409,7 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
 pa_status pa_paged_attention_decode_prefix(void *out, const void *query, void *key_cache,
                                            void *value_cache, const void *new_key,
                                            const void *new_value, const int64_t *slot_mapping,
-                                           const int32_t *block_tables,
+                                           const int64_t *cow_src, const int32_t *block_tables,
                                            const int32_t *context_lens, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t num_kv_heads,
                                            int32_t head_dim, int32_t block_size,
@@ -396,7 +423,7 @@ pa_status pa_paged_attention_decode_prefix(void *out, const void *query, void *k
   if (prefix_len <= 0)
     return pa_fail(PA_ERR_INVALID_ARG, "%s: prefix_len must be positive", fn);
   return decode_call(fn, out, query, key_cache, value_cache, new_key, new_value, slot_mapping,
-                     block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     cow_src, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                      PA_PARTITION_BALANCED, kv_dtype, out_dtype, flags, workspace,
                      workspace_bytes, stream, prefix_len);
@@ -422,14 +449,14 @@ size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q
 
 pa_status pa_paged_attention_decode_append(
     void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
-    const void *new_value, const int64_t *slot_mapping, const int32_t *block_tables,
-    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    const void *new_value, const int64_t *slot_mapping, const int64_t *cow_src,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
     int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
     pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
   pa_clear_error();
   return decode_call("pa_paged_attention_decode_append", out, query, key_cache, value_cache,
-                     new_key, new_value, slot_mapping, block_tables, context_lens, num_seqs,
+                     new_key, new_value, slot_mapping, cow_src, block_tables, context_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, partition_size, kv_dtype, out_dtype,
                      flags, workspace, workspace_bytes, stream);

@@ -237,6 +237,11 @@ struct Params {
   const void *new_key;
   const void *new_value;
   const int64_t *slots;
+  // Copy-on-write inside the launch (null: none): cow_src[i] >= 0 is the
+  // block whose contents sequence i's last block (the new token's block,
+  // slots[i] / block_size) takes.  The attention reads cow_src[i] in its
+  // place, and the launch copies it over before storing the new token.
+  const int64_t *cow_src;
   float *ws_max, *ws_sum, *ws_acc;   // partial rows: [piece * gu + head in unit]
   int32_t *seg_units;                // balanced: per segment, first and last owning wave
   int32_t *seg_cnt;                  // balanced: per segment, chunks merged so far (merge)
@@ -311,11 +316,16 @@ __device__ __forceinline__ bool appends_in(const Piece &pc, int kt) {
 // order, so the chunk after the current one is requested as soon as the
 // current one is entered.  Entries outside [0, num_blocks) are replaced by
 // block 0, so a corrupt table can give a wrong row but never an
-// out-of-bounds access.
+// out-of-bounds access.  With copy-on-write inside the launch, a
+// sequence's last block is read from its copy source instead (sub_blk,
+// sub_phys), by whichever piece reads it: a block of more than 16 tokens
+// can be split between two pieces.
 struct TableReader {
   const int32_t *row;
   int first, count;
   int chunk, vals, vals_next;
+  int sub_blk;
+  int64_t sub_phys;
 
   __device__ __forceinline__ int fetch(int c) const {
     const int idx = (c << 6) + lane_id();
@@ -323,16 +333,28 @@ struct TableReader {
   }
 
   // Request the first two chunks (no wait: the values are used later).
-  __device__ __forceinline__ void start(const Params &p, const Piece &pc, int bs) {
+  // cow: apply the copy sources (the per-sequence pieces, not the shared
+  // prefix's, which never holds a new token's block).
+  __device__ __forceinline__ void start(const Params &p, const Piece &pc, int bs,
+                                        bool cow = true) {
     row = p.block_tables + (int64_t)pc.seq * p.max_blocks_per_seq;
     first = pc.t0 / bs;
     count = (pc.t1 + bs - 1) / bs - first;
     chunk = 0;
     vals = fetch(0);
     vals_next = count > 64 ? fetch(1) : 0;
+    sub_blk = -1;
+    sub_phys = 0;
+    if (cow && p.cow_src != nullptr) {
+      sub_phys = p.cow_src[pc.seq];
+      const int last = (seq_len(p, pc.seq) - 1) / bs;   // the sequence's last block
+      if (sub_phys >= 0 && sub_phys < p.num_blocks && last >= first && last < first + count)
+        sub_blk = last;
+    }
   }
 
-  __device__ __forceinline__ int phys(int blk, int64_t num_blocks) {  // absolute logical block
+  __device__ __forceinline__ int64_t phys(int blk, int64_t num_blocks) {  // absolute logical block
+    if (blk == sub_blk) return sub_phys;
     const int rel = blk - first;
     const int c = rel >> 6;
     if (c != chunk) {
@@ -865,7 +887,10 @@ struct OnePiece {
 
 // The appending variant's cache write: each new token's K and V go into its
 // slot, for every sequence with a slot in the pool, as reshape_and_cache
-// writes them.  No wave of the launch reads these bytes from memory (the
+// writes them.  With copy-on-write inside the launch, the (sequence, KV
+// head)'s part of the copy source block is first copied over the slot's
+// block, as copy_blocks copies it (the source is never written here, and
+// the slot's block is read by no wave: its reader reads the source).  No wave of the launch reads these bytes from memory (the
 // tile holding a new token is patched in registers), so the stores wait
 // until the wave has finished its pieces: stores issued between the reads
 // slow the reads of every wave.  Wave w of n stores the (sequence, KV head)
@@ -887,6 +912,21 @@ __device__ __forceinline__ void store_new_tokens(const Params &p, int64_t w, int
     const int64_t base = (slot / BS * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
     const KV *nk = static_cast<const KV *>(p.new_key) + j * D;
     const KV *nv = static_cast<const KV *>(p.new_value) + j * D;
+    const int64_t src = p.cow_src != nullptr ? p.cow_src[seq] : -1;
+    if (src >= 0 && src < p.num_blocks && src != slot / BS) {
+      const int64_t sbase = (src * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
+      const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.key_cache) + sbase);
+      const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.value_cache) + sbase);
+      u32x4 *kd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.key_cache) + base);
+      u32x4 *vd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.value_cache) + base);
+      for (int i = lane; i < D * BS / X; i += 64) {
+        const u32x4 a = ks[i], b = vs[i];
+        kd[i] = a;
+        vd[i] = b;
+      }
+      // The token's stores below overwrite part of these: let these land first.
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     KV *kc = reinterpret_cast<KV *>(p.key_cache) + base + o * X;
     KV *vc = reinterpret_cast<KV *>(p.value_cache) + base + (o / 16) * D * 16 + o % 16;
     for (int c = lane; c < D / X; c += 64)   // key chunk c: x features of the token
@@ -1167,7 +1207,7 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
   }
   const Piece pc{0, 0, t_lo * 16, t_hi * 16, false, false, 0, -1};
   TableReader tab;
-  tab.start(p, pc, BS);
+  tab.start(p, pc, BS, false);
   const int64_t head_off = (int64_t)h * D * BS;
   int lk = t_lo, ck = t_lo;
   auto load = [&](Tile &tl) -> bool {
@@ -1845,6 +1885,7 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.new_key = a.new_key;
   p.new_value = a.new_value;
   p.slots = a.slots;
+  p.cow_src = a.slots != nullptr ? a.cow_src : nullptr;
   p.ws_max = a.ws_max;
   p.ws_sum = a.ws_sum;
   p.ws_acc = a.ws_acc;

@@ -20,6 +20,7 @@ struct DecodeArgs {
   // Appending variant: new token per sequence and its slot (null otherwise).
   const void *new_key, *new_value;
   const int64_t *slots;
+  const int64_t *cow_src;   // copy-on-write inside the launch (null: none)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int64_t num_blocks;
   int32_t max_context_len;

@@ -50,6 +50,13 @@ class DecodeStep:
     # Tokens every sequence shares in the same blocks (0: none); when set,
     # the attention reads them once for all sequences.
     prefix_len: int = 0
+    # Copy-on-write sources per sequence (int64 [B], -1: none) when every
+    # copy pair is a sequence's new-token block, else None.
+    cow_src: Optional[object] = None
+    # With the in-launch write, copy the pairs inside the attention launch
+    # too (True or None, the default, when cow_src exists) or with
+    # copy_blocks first (False).
+    cow_fused: Optional[bool] = None
 
     @property
     def num_pairs(self) -> int:
@@ -80,9 +87,11 @@ class DecodeStep:
                                          device=self.query.device)
         return self
 
-    def attend(self, stream=None, append=False):
+    def attend(self, stream=None, append=False, cow=False):
         extra = dict(new_key=self.new_key, new_value=self.new_value,
                      slot_mapping=self.slot_mapping) if append else {}
+        if cow:
+            extra["cow_src"] = self.cow_src
         if self.prefix_len:
             B.paged_attention_decode_prefix(
                 self.out, self.query, self.key_cache, self.value_cache, self.block_tables,
@@ -107,6 +116,14 @@ class DecodeStep:
     def uses_fused_write(self) -> bool:
         return True if self.fused is None else self.fused
 
+    @property
+    def uses_fused_copy(self) -> bool:
+        """Copy-on-write inside the attention launch: with the in-launch
+        write, when there are pairs and each is a sequence's new-token
+        block."""
+        return (self.uses_fused_write and self.num_pairs > 0 and self.cow_src is not None
+                and self.cow_fused is not False)
+
     def capture(self):
         """Record run() into a HIP graph (torch.cuda.CUDAGraph); replay()
         then repeats the step's launches with one call.  The graph reads
@@ -129,8 +146,12 @@ class DecodeStep:
         return self.out
 
     def run(self, stream=None):
-        """copy_blocks, then either one launch that writes the new tokens and
-        attends (fused) or reshape_and_cache followed by attention."""
+        """One launch that copies the shared blocks, writes the new tokens and
+        attends (fused); or copy_blocks first, then that launch without the
+        copies; or copy_blocks, reshape_and_cache and attention."""
+        if self.uses_fused_copy:
+            self.attend(stream, append=True, cow=True)
+            return self.out
         self.copy(stream)
         if self.uses_fused_write:
             self.attend(stream, append=True)
@@ -154,9 +175,32 @@ def _finish(query, key_cache, value_cache, new_key, new_value, slots, pairs, tab
     nbytes = B.paged_attention_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
                                                head_dim, mcl, partition_size, query.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
-    return DecodeStep(query, key_cache, value_cache, new_key, new_value, t_slots, t_pairs, t_tab,
+    step = DecodeStep(query, key_cache, value_cache, new_key, new_value, t_slots, t_pairs, t_tab,
                       t_lens, out, ws, num_kv_heads, head_dim, block_size, num_blocks, mcl, scale,
                       partition_size)
+    step.cow_src = _cow_sources(slots, pairs, block_size, dev)
+    return step
+
+
+def _cow_sources(slots, pairs, block_size, dev):
+    """Per-sequence copy sources (int64 [B], -1: none) when every pair's
+    destination is exactly one sequence's new-token block, else None."""
+    import torch
+    slots = np.asarray(slots, dtype=np.int64)
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if pairs.shape[0] == 0:
+        return None
+    src = np.full(slots.shape[0], -1, np.int64)
+    seq_of_block = {}
+    for i, sl in enumerate(slots):
+        if sl >= 0:
+            seq_of_block.setdefault(int(sl) // block_size, []).append(i)
+    for s_blk, d_blk in pairs:
+        owners = seq_of_block.get(int(d_blk), [])
+        if len(owners) != 1 or src[owners[0]] >= 0:
+            return None
+        src[owners[0]] = s_blk
+    return torch.as_tensor(src).to(dev)
 
 
 def step_from_case(case, partition_size: int, out_dtype=None) -> DecodeStep:

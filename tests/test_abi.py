@@ -68,7 +68,7 @@ def test_decode_rejects_bad_arguments_before_launch(kw, status):
 def test_append_needs_all_three_new_token_pointers():
     lib = pa.load()
     base = dict(out=16, query=32, key_cache=48, value_cache=64, new_key=NULL, new_value=NULL,
-                slot_mapping=NULL, block_tables=8, context_lens=8, num_seqs=1, num_q_heads=8,
+                slot_mapping=NULL, cow_src=NULL, block_tables=8, context_lens=8, num_seqs=1, num_q_heads=8,
                 num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4,
                 num_blocks=16, max_context_len=64, scale=0.1, partition_size=0,
                 kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16, flags=0, workspace=NULL,
@@ -82,9 +82,24 @@ def test_append_needs_all_three_new_token_pointers():
     assert lib.pa_paged_attention_decode_append(*a.values()) == pa.PA_OK
 
 
+def test_cow_src_needs_the_new_tokens():
+    """Copy-on-write inside the launch is part of the new tokens' write."""
+    lib = pa.load()
+    a = dict(out=16, query=32, key_cache=48, value_cache=64, new_key=NULL, new_value=NULL,
+             slot_mapping=NULL, cow_src=8, block_tables=8, context_lens=8, num_seqs=1,
+             num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4,
+             num_blocks=16, max_context_len=64, scale=0.1, partition_size=0,
+             kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16, flags=0, workspace=NULL,
+             workspace_bytes=0, stream=NULL)
+    assert lib.pa_paged_attention_decode_append(*a.values()) == pa.PA_ERR_INVALID_ARG
+    assert b"cow_src" in lib.pa_last_error()
+    assert _prefix(lib, cow_src=8) == pa.PA_ERR_INVALID_ARG
+    assert b"cow_src" in lib.pa_last_error()
+
+
 def _prefix(lib, **kw):
     a = dict(out=16, query=32, key_cache=48, value_cache=64, new_key=NULL, new_value=NULL,
-             slot_mapping=NULL, block_tables=8, context_lens=8, num_seqs=2, num_q_heads=8,
+             slot_mapping=NULL, cow_src=NULL, block_tables=8, context_lens=8, num_seqs=2, num_q_heads=8,
              num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4,
              num_blocks=16, max_context_len=64, scale=0.1, prefix_len=32,
              kv_dtype=pa.PA_BF16, out_dtype=pa.PA_BF16, flags=0, workspace=NULL,
