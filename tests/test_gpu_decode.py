@@ -357,3 +357,34 @@ def test_balanced_results_do_not_depend_on_xcd_weights(gpu):
                 assert max_abs_err(a, ref) <= TOL[case.dtype]
         finally:
             gpu.set_balance_weights(None)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(num_q_heads=8, num_kv_heads=8)])
+def test_workspace_contents_need_no_initialisation(gpu, kw):
+    """The merge's counters and per-wave records live in the caller's
+    workspace: random bytes there before the call, or a workspace used by
+    another call just before, must give the same bits as a zeroed one."""
+    rng = np.random.default_rng(3)
+    lens = tuple(int(x) for x in rng.integers(0, 65, size=299)) + (30000,)
+    case = W.make_case("70b", device="cuda", batch=300, lens=lens, **kw)
+    q = case.query
+    tab, ln = to_dev(case.block_tables), to_dev(case.context_lens)
+    mcl = int(case.context_lens.max())
+    nbytes = gpu.paged_attention_workspace_bytes(q.shape[0], q.shape[1], case.num_kv_heads,
+                                                 q.shape[2], mcl, BAL, q.dtype)
+    outs = []
+    for fill in ("zero", "random", "reused"):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda"))
+        out = torch.empty_like(q)
+        for _ in range(2 if fill == "reused" else 1):   # the second call sees the first's words
+            gpu.paged_attention_decode(out, q, case.key_cache, case.value_cache, tab, ln,
+                                       num_kv_heads=case.num_kv_heads,
+                                       block_size=case.block_size, max_context_len=mcl,
+                                       scale=case.scale, partition_size=BAL,
+                                       num_blocks=case.num_blocks, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    _check(gpu, case, BAL, idx=[0, 1, 299])
