@@ -1630,6 +1630,15 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
     store_rows(out, nh, false);
   };
 
+  // The segment the main kernel's wave b started in and its owners, for
+  // the chunks c >= 1 below: requested first, so that these loads overlap
+  // the chunk-0 work instead of following it.
+  int gb = -1, gu0 = 0, gu1 = 0;
+  if (b < p.waves) gb = p.wave_segs[b];
+  if (gb >= 0) {
+    gu0 = p.seg_units[2 * (int64_t)gb];
+    gu1 = p.seg_units[2 * (int64_t)gb + 1];
+  }
   // Chunk 0 of segment b, or its zero rows.
   if (b < segs) {
     // The owning waves are requested with the length (stale, and unused,
@@ -1648,16 +1657,12 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
   }
   // A chunk c >= 1 this wave leads: in the segment the main kernel's wave b
   // started in.
-  if (b < p.waves) {
+  if (gb >= 0) {
     const int j = b / p.xsplit;
-    const int g = p.wave_segs[b];
-    if (g >= 0) {
-      const int u0 = p.seg_units[2 * (int64_t)g], u1 = p.seg_units[2 * (int64_t)g + 1];
-      const int n = u1 - u0 + 1;
-      if (n > 4 * KB && j > u0 && j <= u1) {   // several chunks, not chunk 0
-        const int C = merge_chunk<KB>(n);
-        if ((j - u0) % C == 0) lead(g, u0, u1, (j - u0) / C);
-      }
+    const int n = gu1 - gu0 + 1;
+    if (n > 4 * KB && j > gu0 && j <= gu1) {   // several chunks, not chunk 0
+      const int C = merge_chunk<KB>(n);
+      if ((j - gu0) % C == 0) lead(gb, gu0, gu1, (j - gu0) / C);
     }
   }
 }
