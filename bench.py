@@ -327,7 +327,7 @@ def copy_calibration(device, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
     ap.add_argument("--partition-size", type=int, default=-1,
