@@ -146,8 +146,9 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
  *                 (no new token: sequence i is attended as is) or the slot
  *                 of position context_lens[i] - 1 in block_tables row i,
  *                 in a block that no other sequence of the call reads or
- *                 writes (true of blocks from pa_seq_append_slot, which
- *                 copies a shared block first).  PA_VALIDATE=1 checks the
+ *                 writes (true of blocks from pa_seq_append_slot, whose
+ *                 copy-on-write pair is copied first: by pa_copy_blocks,
+ *                 or by this launch through cow_src).  PA_VALIDATE=1 checks the
  *                 position; a slot outside the pool is skipped like a
  *                 negative one.
  *  cow_src        NULL, or int64 [num_seqs] (device): copy-on-write inside
@@ -170,9 +171,10 @@ pa_status pa_paged_attention_decode(void *out, const void *query, const void *ke
 pa_status pa_paged_attention_decode_append(
     void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
     const void *new_value, const int64_t *slot_mapping, const int64_t *cow_src,
-    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-    int32_t max_context_len, float scale, int32_t partition_size, pa_dtype kv_dtype,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, pa_dtype kv_dtype,
     pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
