@@ -171,3 +171,54 @@ def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size):
                                  head_dim=d, block_size=block_size, scale=d ** -0.5,
                                  num_blocks=N, threads=16)
     assert max_abs_err(outs[0], ref) <= TOL["bf16"]
+
+
+def test_deep_validation_checks_the_copy_sources(gpu, monkeypatch):
+    """PA_VALIDATE=1: a copy source must be another block of the pool, for a
+    sequence with a new token, and any in-place write into it must be at the
+    copier's own offset; a bad one is refused before any launch."""
+    from paged_kv_cache_305_amd import _binding as B
+    from paged_kv_cache_305_amd.step import _finish
+    bs, hq, hkv, d = 16, 8, 2, 128
+    a = B.BlockAllocator(32, bs)
+    for i, n in enumerate((20, 37)):
+        a.create(i, n)
+        a.fork(i, 2 + i)
+    slots, pairs = np.empty(4, np.int64), []
+    for i in range(4):                 # parents copy, children write their source in place
+        s_, src, dst = a.append_slot(i)
+        slots[i] = s_
+        if src >= 0:
+            pairs.append((src, dst))
+    lens = np.array([a.seq_len(i) for i in range(4)], np.int64)
+    tables, lens32 = a.build_block_tables(list(range(4)), int(-(-lens.max() // bs)))
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device="cuda").to(torch.bfloat16)
+    kc, vc = randn(32, hkv, bs * d), randn(32, hkv, bs * d)
+    q, nk, nv = randn(4, hq, d), randn(4, hkv, d), randn(4, hkv, d)
+    step = _finish(q, kc, vc, nk, nv, slots, np.array(pairs, np.int64), tables, lens32,
+                   num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=32, scale=d ** -0.5,
+                   partition_size=-1)
+    assert step.uses_fused_copy
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    good = step.cow_src.clone()
+    step.run()                          # consistent sources pass
+    torch.cuda.synchronize()
+    src = good.cpu().numpy()
+    bad_cases = []
+    b = src.copy(); b[0] = slots[0] // bs; bad_cases.append(b)            # its own block
+    b = src.copy(); b[0] = 32; bad_cases.append(b)                        # outside the pool
+    child_block = slots[3] // bs        # sequence 1's source, written in place by sequence 3
+    b = src.copy(); b[0] = child_block; bad_cases.append(b)               # another offset
+    for b in bad_cases:
+        step.cow_src = torch.as_tensor(b).cuda()
+        with pytest.raises(gpu.PagedAttnError) as e:
+            step.run()
+        assert e.value.status == gpu.PA_ERR_INVALID_ARG
+    step.cow_src = good
+    step.slot_mapping = step.slot_mapping.clone()
+    step.slot_mapping[0] = -1           # a source for a sequence without a new token
+    with pytest.raises(gpu.PagedAttnError) as e:
+        step.run()
+    assert e.value.status == gpu.PA_ERR_INVALID_ARG
