@@ -111,9 +111,18 @@ def test_decode_step_writes_then_attends(gpu, name, kw, ps, fused):
     assert max_abs_err(step.out[torch.as_tensor(idx, device="cuda")], ref) <= TOL[case.dtype]
 
 
+BEAM_SHAPES = [
+    dict(hq=16, hkv=4, d=128, dtype=torch.bfloat16),   # MFMA body
+    dict(hq=8, hkv=8, d=128, dtype=torch.bfloat16),    # VALU body (one head per unit)
+    dict(hq=8, hkv=2, d=128, dtype=torch.float32),     # VALU body, fp32 pools
+    dict(hq=12, hkv=4, d=64, dtype=torch.bfloat16),    # d 64
+]
+
+
 @pytest.mark.parametrize("ps", [-1, 0, 64])
-@pytest.mark.parametrize("block_size", [16, 32])
-def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size):
+@pytest.mark.parametrize("block_size", [16, 32, 64])
+@pytest.mark.parametrize("shape", range(len(BEAM_SHAPES)))
+def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size, shape):
     """Beam-search forks: every prompt (lengths not multiples of the block
     size) is forked and both parent and child append.  The parent, first in
     id order, copies the shared partial block; the child then writes into
@@ -122,8 +131,9 @@ def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size):
     oracle within tolerance, and both must equal the copy_blocks path."""
     from paged_kv_cache_305_amd import _binding as B
     from paged_kv_cache_305_amd.step import _finish
-    rng = np.random.default_rng(block_size + ps)
-    n_par, hq, hkv, d = 12, 16, 4, 128
+    rng = np.random.default_rng(block_size + ps + 100 * shape)
+    sh = BEAM_SHAPES[shape]
+    n_par, hq, hkv, d, dt = 12, sh["hq"], sh["hkv"], sh["d"], sh["dtype"]
     prompts = rng.integers(1, 300, size=n_par)
     prompts[prompts % block_size == 0] += 1
     N = int(sum(-(-int(L) // block_size) + 2 for L in prompts)) + 8
@@ -142,8 +152,8 @@ def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size):
     lens = np.array([a.seq_len(i) for i in seqs], np.int64)
     tables, lens32 = a.build_block_tables(seqs, int(-(-lens.max() // block_size)))
     gen = torch.Generator(device="cuda").manual_seed(5)
-    def randn(*shape):
-        return torch.randn(*shape, generator=gen, device="cuda").to(torch.bfloat16)
+    def randn(*dims):
+        return torch.randn(*dims, generator=gen, device="cuda").to(dt)
     kc, vc = randn(N, hkv, block_size * d), randn(N, hkv, block_size * d)
     q, nk, nv = randn(len(seqs), hq, d), randn(len(seqs), hkv, d), randn(len(seqs), hkv, d)
     kc_h, vc_h = W.host_array(kc).copy(), W.host_array(vc).copy()
@@ -170,7 +180,7 @@ def test_beam_forks_copy_on_write_inside_the_launch(gpu, ps, block_size):
     ref = oracle.paged_attention(W.host_array(q), kc_h, vc_h, tables, lens32, num_kv_heads=hkv,
                                  head_dim=d, block_size=block_size, scale=d ** -0.5,
                                  num_blocks=N, threads=16)
-    assert max_abs_err(outs[0], ref) <= TOL["bf16"]
+    assert max_abs_err(outs[0], ref) <= TOL["bf16" if dt == torch.bfloat16 else "fp32"]
 
 
 def test_deep_validation_checks_the_copy_sources(gpu, monkeypatch):
