@@ -65,7 +65,7 @@ BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident);
 #define PA_PREFIX_ROW_TILES 2
 #endif
 #ifndef PA_PREFIX_WAVES_PER_CU
-#define PA_PREFIX_WAVES_PER_CU 4
+#define PA_PREFIX_WAVES_PER_CU 3
 #endif
 constexpr int kPrefixRowTiles = PA_PREFIX_ROW_TILES;     // 16-row tiles per wave
 constexpr int kPrefixWavesPerCU = PA_PREFIX_WAVES_PER_CU;
