@@ -229,8 +229,8 @@ pa_status pa_set_timing_events(void *before_main, void *after_main);
 /* Tile shares of the balanced split (partition_size < 0), one weight per XCD
  * in workgroup dispatch order (workgroup w runs on XCD w mod 8): each wave's
  * range of tiles is proportional to its XCD's weight.  Default
- * {110,100,110,100,110,100,110,100}: on MI355X, waves on even-numbered XCDs
- * stream about 10% faster than waves on odd-numbered ones.  weights == NULL
+ * {115,100,115,100,115,100,115,100}: on MI355X, waves on even-numbered XCDs
+ * stream 10-15% faster than waves on odd-numbered ones.  weights == NULL
  * restores the default; otherwise n must be 8 and each weight in [1, 1000].
  * Process-wide.  Weights move the piece boundaries, so outputs may change in
  * their last bits (within the attention tolerance); for fixed weights,

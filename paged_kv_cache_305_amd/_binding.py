@@ -220,7 +220,7 @@ def set_timing_events(before_main=None, after_main=None):
 
 def set_balance_weights(weights=None):
     """Per-XCD tile shares of the balanced split (8 ints in [1, 1000]); None restores
-    the default (even-numbered XCDs 110, odd 100)."""
+    the default (even-numbered XCDs 115, odd 100)."""
     if weights is None:
         _check(load().pa_set_balance_weights(None, 0))
         return
