@@ -343,6 +343,9 @@ def main():
                     help="copy-on-write pairs: inside the attention launch with the new tokens "
                          "(fused, when each pair is a new-token block) or with copy_blocks "
                          "first (separate); auto = fused")
+    ap.add_argument("--xcd-weights", default=None,
+                    help="per-XCD tile shares of the balanced split, 8 comma-separated ints, or "
+                         "two (even,odd) repeated over the 8 XCDs (default: the library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--block-size", type=int, default=None,
@@ -378,6 +381,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pa.load()
+    if args.xcd_weights:
+        wts = [int(x) for x in args.xcd_weights.split(",")]
+        pa.set_balance_weights(wts * 4 if len(wts) == 2 else wts)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     if args.copy_calibration:
@@ -463,7 +469,7 @@ def main():
                 traffic=counter_traffic(args.workload, args.partition_size)
                 if args.block_size in (None, W.CONFIGS.get(args.workload, {}).get("block_size")) and args.batch is None
                 and args.table_order == "random" and args.cache_write == "auto"
-                and args.cow == "auto" and not args.no_prefix else None,
+                and args.cow == "auto" and not args.no_prefix and not args.xcd_weights else None,
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
                 kernel_source_digest=kernel_source_digest())
     result = {
