@@ -987,12 +987,25 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Extra tiles each nonempty segment counts for in the balanced split, placed
+// after its real tiles on the tile line: a range that touches more segments
+// (more pieces: query loads, table starts, partial rows) gets fewer tiles.
+// No range ever holds a virtual tile between two real tiles of a segment,
+// so a segment's owning waves stay consecutive.
+#ifndef PA_SEGMENT_COST
+#define PA_SEGMENT_COST 4
+#endif
+constexpr int kSegmentCost = PA_SEGMENT_COST;
+
+// Extent of a segment of n real tiles on the balanced split's tile line.
+__device__ __forceinline__ int seg_extent(int n) { return n > 0 ? n + kSegmentCost : 0; }
+
 // Tiles of one unit summed over all sequences: sum_i ceil(L_i / 16).
 __device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
   int64_t tot = 0;
   for (int c = 0; c < p.num_seqs; c += 64) {
     const int i = c + lane_id();
-    tot += wave_sum(i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0);
+    tot += wave_sum(i < p.num_seqs ? seg_extent(own_tiles(p, seq_len(p, i))) : 0);
   }
   return tot;
 }
@@ -1057,46 +1070,54 @@ struct RangePieces {
 
   __device__ void defer_first() {
     has_deferred = false;
-    if (a > 0 && te - t > n_seq - a) {
+    if (a > 0 && a < n_seq && te - t > seg_extent(n_seq) - a) {
       next(deferred);
       has_deferred = true;
     }
   }
 
+  // The next piece: the real tiles of the next segment the range covers
+  // (positions a.. of its extent; a range may cover only a segment's
+  // virtual tiles, which give no piece).
   __device__ bool next(Piece &out) {
-    if (t >= te) {
-      if (!has_deferred) return false;
-      has_deferred = false;
-      out = deferred;
-      return true;
-    }
-    const int len = (int)min((int64_t)(n_seq - a), te - t);
-    const int b = a + len;
-    const int u = x + p->xsplit * k;
-    const int64_t g = (int64_t)seq * p->units + u;
-    if (lane_id() == 0) {
-      if (a == 0) {
-        p->seg_units[2 * g] = (int32_t)unit;
-        if (p->seg_cnt) p->seg_cnt[g] = 0;   // the merge counts this segment's chunks
-      }
-      if (b == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
-    }
-    const int pt = p->prefix_tiles;
-    out = Piece{seq, u, (a + pt) * 16, min((b + pt) * 16, L), pt == 0 && a == 0 && b == n_seq,
-                b == n_seq, id_base + (int64_t)seq * ux + k + unit, -1};
-    t += len;
-    a = 0;
-    if (t < te && ++k == ux) {
-      k = 0;
-      do {
-        if (++seq >= p->num_seqs) {   // unreachable while t < te
-          t = te;
-          break;
+    while (t < te) {
+      const int ext = seg_extent(n_seq);
+      const int len = (int)min((int64_t)(ext - a), te - t);
+      const int ra = min(a, n_seq), rb = min(a + len, n_seq);   // real tiles [ra, rb)
+      const int u = x + p->xsplit * k;
+      const int64_t g = (int64_t)seq * p->units + u;
+      const bool has = ra < rb;
+      if (has) {
+        if (lane_id() == 0) {
+          if (ra == 0) {
+            p->seg_units[2 * g] = (int32_t)unit;
+            if (p->seg_cnt) p->seg_cnt[g] = 0;   // the merge counts this segment's chunks
+          }
+          if (rb == n_seq) p->seg_units[2 * g + 1] = (int32_t)unit;
         }
-        L = lens.get(*p, seq);
-        n_seq = own_tiles(*p, L);
-      } while (n_seq == 0);
+        const int pt = p->prefix_tiles;
+        out = Piece{seq, u, (ra + pt) * 16, min((rb + pt) * 16, L),
+                    pt == 0 && ra == 0 && rb == n_seq, rb == n_seq,
+                    id_base + (int64_t)seq * ux + k + unit, -1};
+      }
+      t += len;
+      a = 0;
+      if (t < te && ++k == ux) {
+        k = 0;
+        do {
+          if (++seq >= p->num_seqs) {   // unreachable while t < te
+            t = te;
+            break;
+          }
+          L = lens.get(*p, seq);
+          n_seq = own_tiles(*p, L);
+        } while (n_seq == 0);
+      }
+      if (has) return true;
     }
+    if (!has_deferred) return false;
+    has_deferred = false;
+    out = deferred;
     return true;
   }
 };
@@ -1131,13 +1152,13 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   for (int c = 0; c < p.num_seqs && gen.seq < 0; c += 64) {
     const int i = c + lane;
     const int n = i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0;
-    const int incl = wave_incl_scan(n);
+    const int incl = wave_incl_scan(seg_extent(n));
     const uint64_t hit = __builtin_amdgcn_ballot_w64((base + incl) * gen.ux > gen.t);
     if (hit) {
       const int l0 = (int)__builtin_ctzll(hit);
       gen.seq = c + l0;
       gen.n_seq = __builtin_amdgcn_readlane(n, l0);
-      seq_first = (base + __builtin_amdgcn_readlane(incl, l0) - gen.n_seq) * gen.ux;
+      seq_first = (base + __builtin_amdgcn_readlane(incl, l0) - seg_extent(gen.n_seq)) * gen.ux;
     }
     base += __builtin_amdgcn_readlane(incl, 63);
   }
@@ -1147,8 +1168,8 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   }
   gen.lens.load(p, gen.seq);
   gen.L = gen.lens.get(p, gen.seq);
-  gen.k = (int)((gen.t - seq_first) / gen.n_seq);
-  gen.a = (int)((gen.t - seq_first) % gen.n_seq);
+  gen.k = (int)((gen.t - seq_first) / seg_extent(gen.n_seq));
+  gen.a = (int)((gen.t - seq_first) % seg_extent(gen.n_seq));
   gen.first_g = (int64_t)gen.seq * p.units + gen.x + p.xsplit * gen.k;
   gen.has_deferred = false;
   gen.defer_first();
