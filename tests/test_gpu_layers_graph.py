@@ -149,3 +149,35 @@ def test_three_layer_step_in_one_graph(gpu):
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e)
+
+
+@pytest.mark.parametrize("kind", ["many_short_one_long", "shared_prefix_copies"])
+def test_graph_replays_of_the_segment_merge_and_in_launch_copies(gpu, kind):
+    """Replays of a captured step equal eager runs when the merge uses its
+    per-segment counters (reset by the main kernel inside the graph, no
+    memset) and when copy-on-write runs inside the attention launch."""
+    from paged_kv_cache_305_amd.step import shared_prefix_step, step_from_case
+    if kind == "many_short_one_long":
+        rng = np.random.default_rng(21)
+        lens = tuple(int(x) for x in rng.integers(0, 65, size=299)) + (30000,)
+        case = W.make_case("70b", device="cuda", batch=300, lens=lens)
+        step = step_from_case(case, partition_size=-1)
+    else:
+        plan = W.shared_plan()
+        tens = W.shared_tensors(plan, device="cuda")
+        step, _ = shared_prefix_step(plan, tens, partition_size=-1, prefix=True)
+        assert step.uses_fused_copy
+    step.capture()
+    gen = torch.Generator(device="cuda").manual_seed(79)
+    for r in range(3):
+        q = torch.randn(step.query.shape, generator=gen, device="cuda").to(step.query.dtype)
+        step.query.copy_(q)
+        eager = step.run().clone()
+        kc, vc = step.key_cache.clone(), step.value_cache.clone()
+        torch.cuda.synchronize()
+        _ = (torch.randn(1 << 20, device="cuda") * 2).sum()      # unrelated eager work
+        step.out.zero_()
+        got = step.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), r
+        assert torch.equal(step.key_cache, kc) and torch.equal(step.value_cache, vc)
