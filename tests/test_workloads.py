@@ -71,3 +71,18 @@ def test_shared_plan_structure():
     needed = 250 + int(sum(-(-int(t) // 16) + 1 for t in p.tails))
     assert p.num_blocks == math.ceil(1.5 * needed)
     assert sorted(p.perm.tolist()) == list(range(p.num_blocks))
+
+
+def test_mixed_workload_has_one_long_context():
+    """The 70B shape with one 131,072-token context at a seeded position:
+    seeded after the five workloads, the other 255 lengths in [128, 4096],
+    exactly the blocks needed."""
+    st = W.case_structure("mixed")
+    assert W.seed_for("mixed") == 310
+    L = st.lengths
+    assert L.shape == (256,) and (L == 131072).sum() == 1
+    others = L[L != 131072]
+    assert others.min() >= 128 and others.max() <= 4096
+    assert st.num_blocks == int(sum(-(-int(x) // 16) for x in L))
+    again = W.case_structure("mixed")
+    assert (again.lengths == L).all() and (again.perm == st.perm).all()
