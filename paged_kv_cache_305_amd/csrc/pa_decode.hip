@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "pa_internal.h"
+#include "pa_launch_map.h"
 
 namespace pa {
 namespace {
@@ -267,7 +268,6 @@ struct Params {
   int pf_chunks, pf_chunk_tiles;   // prefix split into chunks of tiles
   int pf_rows;                     // query rows per KV head: num_seqs * group
   int pf_waves;                    // prefix waves of the launch
-  int pf_mix;                      // tail / prefix waves dealt alternately, per kind
   float *pf_max, *pf_sum, *pf_acc; // partials [chunk][KV head][row]
 };
 
@@ -1310,27 +1310,20 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
 // Shared prefix and per-sequence tails in one launch: prefix waves wait on
 // cache-level reads of the few prefix blocks, tail waves stream the
 // sequences' own blocks from HBM, so the two kinds overlap.  Workgroups are
-// dealt in runs of 8, alternating tail / prefix while both kinds remain,
-// then the rest of the larger kind; each wave's index within its kind
-// equals its workgroup id mod 8, which keeps both kinds' XCD placement.
+// dealt in runs of 8, alternating tail / prefix while both kinds have a
+// run left, then the remaining tail waves and the remaining prefix waves
+// (mixed_wave): every wave of each kind runs exactly once.
 template <class Body>
 __global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_prefix_tails(Params p) {
   __shared__ float p_lds[2][16];
-  const int b = (int)blockIdx.x, m = p.pf_mix;
-  bool tail;
-  int vb;
-  if (b < 2 * m) {
-    tail = ((b >> 3) & 1) == 0;
-    vb = ((b >> 4) << 3) | (b & 7);
+  const MixedWave mw = mixed_wave((int)blockIdx.x, p.waves, p.pf_waves);
+  if (mw.tail) {
+    if (mw.index >= p.waves) return;   // only if the grid were larger than both kinds
+    run_balanced<Body>(p, p_lds, mw.index);
+    store_new_tokens<Body>(p, mw.index, p.waves);
   } else {
-    tail = p.waves > p.pf_waves;
-    vb = m + (b - 2 * m);
-  }
-  if (tail) {
-    run_balanced<Body>(p, p_lds, vb);
-    store_new_tokens<Body>(p, vb, p.waves);
-  } else {
-    run_prefix<Body::kHeadDim, Body::kBlockSize>(p, p_lds, vb);
+    if (mw.index >= p.pf_waves) return;
+    run_prefix<Body::kHeadDim, Body::kBlockSize>(p, p_lds, mw.index);
   }
 }
 
@@ -1724,8 +1717,6 @@ hipError_t launch_balanced(const DecodeArgs &a, Params &p, hipStream_t st) {
   for (int i = 0; i < 8; ++i) p.xcd_prefix[i + 1] = p.xcd_prefix[i] + a.xcd_weights[i];
   if constexpr (pf_ok) {
     if (pf) {
-      const int m = plan.waves < p.pf_waves ? plan.waves : p.pf_waves;
-      p.pf_mix = m - m % 8;
       const int64_t grid = (int64_t)plan.waves + p.pf_waves;
       if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
       hipLaunchKernelGGL((decode_prefix_tails<Body>), dim3((unsigned)grid), dim3(64), 0, st, p);
@@ -1937,7 +1928,7 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.id_stride = 0;
   p.scale_log2e = a.scale * kLog2e;
   p.prefix_tiles = a.prefix_len / 16;
-  p.pf_chunks = p.pf_chunk_tiles = p.pf_rows = p.pf_waves = p.pf_mix = 0;
+  p.pf_chunks = p.pf_chunk_tiles = p.pf_rows = p.pf_waves = 0;
   p.pf_max = a.pf_max;
   p.pf_sum = a.pf_sum;
   p.pf_acc = a.pf_acc;

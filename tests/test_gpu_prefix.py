@@ -56,6 +56,11 @@ CASES = [
     ("70b", 2, (0, 31, 100), dict(block_size=32)),
     ("70b", 1, (1, 65, 200), dict(block_size=64)),
     ("70b", 40, tuple(range(0, 330, 11)), {}),                   # 30 sequences, many chunks
+    # 12 prefix waves (not a multiple of 8) beside a full set of tail
+    # waves: the 4 prefix waves past the alternating runs must still run.
+    ("7b", 3, (1000, 990, 1013, 1003), dict(num_q_heads=28, num_kv_heads=4)),   # G = 7
+    # Fewer than 8 waves of each kind: no alternating runs at all.
+    ("7b", 1, (3, 10), dict(num_q_heads=8, num_kv_heads=2)),
 ]
 
 
