@@ -142,15 +142,14 @@ def test_more_new_tokens_than_waves(gpu, name, batch):
     _check_case(gpu, case, BAL)
 
 
-def test_full_size_steps_on_sampled_sequences(gpu):
-    for name in ("7b", "70b"):
-        case = W.make_case(name, device="cuda")
-        out, kc, vc = _run(gpu, case, BAL, case.slot_mapping, fused=True)
-        idx = np.sort(np.random.default_rng(5).choice(case.batch, size=6, replace=False))
-        ref, kc_o, vc_o = _oracle(case, case.slot_mapping, idx=idx)
-        assert W.host_array(kc).tobytes() == kc_o.tobytes()
-        assert W.host_array(vc).tobytes() == vc_o.tobytes()
-        assert max_abs_err(out[torch.as_tensor(idx, device="cuda")], ref) <= TOL[case.dtype]
+@pytest.mark.parametrize("name", ["7b", "70b", "long", "mixed"])
+def test_full_size_steps_on_every_row(gpu, name):
+    case = W.make_case(name, device="cuda")
+    out, kc, vc = _run(gpu, case, BAL, case.slot_mapping, fused=True)
+    ref, kc_o, vc_o = _oracle(case, case.slot_mapping)
+    assert W.host_array(kc).tobytes() == kc_o.tobytes()
+    assert W.host_array(vc).tobytes() == vc_o.tobytes()
+    assert max_abs_err(out, ref) <= TOL[case.dtype]
 
 
 def test_deep_validation_rejects_a_slot_off_the_last_position(gpu, monkeypatch):

@@ -101,14 +101,12 @@ def test_decode_step_writes_then_attends(gpu, name, kw, ps, fused):
                              num_blocks=case.num_blocks)
     assert W.host_array(case.key_cache).tobytes() == kc_h.tobytes()
     assert W.host_array(case.value_cache).tobytes() == vc_h.tobytes()
-    idx = np.sort(np.random.default_rng(11).choice(case.batch, size=min(5, case.batch),
-                                                   replace=False))
-    ref = oracle.paged_attention(W.host_array(case.query)[idx], kc_h, vc_h,
-                                 case.block_tables[idx], case.context_lens[idx],
+    ref = oracle.paged_attention(W.host_array(case.query), kc_h, vc_h,
+                                 case.block_tables, case.context_lens,
                                  num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
                                  block_size=case.block_size, scale=case.scale,
                                  num_blocks=case.num_blocks, threads=16)
-    assert max_abs_err(step.out[torch.as_tensor(idx, device="cuda")], ref) <= TOL[case.dtype]
+    assert max_abs_err(step.out, ref) <= TOL[case.dtype]
 
 
 BEAM_SHAPES = [
