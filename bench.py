@@ -10,13 +10,26 @@ several pieces).  Each sequence's new token is written into its slot either
 by that launch or by reshape_and_cache just before it (--cache-write; by
 default the launch writes).
 
+The default run times the 70B-shaped GQA step (the headline line) and, in
+the same process, the 7B-shaped, long-context (block sizes 16 and 32),
+shared-prefix and tiny steps, each reported under "workloads" with its own
+timing, roofline and parity.  It also measures the GPU's streaming-read and
+4 KiB-block gather ceilings (libpaprobe.so), so every kernel rate is given
+as a fraction of the nominal 8 TB/s and of what the memory system delivers.
+
 Timing: W warm-up steps, then K timed steps.  Before each step a 1 GiB
 buffer is read to evict the L2s and the Infinity Cache (outside the
 events); reading leaves only clean lines behind, so no write-back of the
-flush competes with the step.  Each step is bracketed by HIP events on the stream the kernels
-run on.  A second pass of K steps brackets the main attention kernel with
-its own pair of events, recorded by the library right around its launch
-(kept out of the first pass: events inside a step lengthen it).
+flush competes with the step.  Each step is bracketed by HIP events on the
+stream the kernels run on.  A second pass of K steps brackets the main
+attention kernel with its own pair of events, recorded by the library right
+around its launch (kept out of the first pass: events inside a step
+lengthen it), and the end of the step with a third.
+
+Parity: after the timed steps, every output row of the step is compared
+with the CPU oracle run on host copies of the same inputs, and the pools
+with the oracle's copy-on-write copies and token writes applied to a
+snapshot taken before the first step (bit for bit).
 
 Output: one JSON line (rank 0).  value = KV bytes read by attention per
 step / mean step time, in GB/s.
@@ -218,6 +231,12 @@ def counter_traffic(workload, ps):
     return t.get("hbm_bytes_per_launch")
 
 
+# ---- the oracle leg: CPU baseline and parity of the timed step -------------
+#
+# The CPU oracle (oracle/) runs only here, after the timed region: once timed
+# on a bounded sample of the step (the CPU baseline), and once over every row
+# of the step to check what the GPU computed.  The timed path never calls it.
+
 def cpu_baseline(step, lens, max_seconds, threads=None):
     """The oracle, as it stands, on this host's cores, over a bounded sample:
     consecutive sequences of the step (wrapping around the batch), in chunks
@@ -254,6 +273,308 @@ def cpu_baseline(step, lens, max_seconds, threads=None):
                 sample="%d sequence-attentions (%.2f passes over the step's %d sequences), fp64 "
                        "gather + naive softmax attention, %d threads" % (
                            done_seqs, done_seqs / B, B, threads))
+
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def step_parity(step, pools_before):
+    """Every output row of the step against the oracle, and the pools bit
+    for bit.  The oracle applies the step's copy-on-write pairs and new
+    tokens to the snapshot taken before the first step, then attends over
+    every sequence of the batch."""
+    import oracle
+    import workloads as W
+    import torch
+    t0 = time.perf_counter()
+    kc, vc = pools_before
+    hkv, d, bs, N = step.num_kv_heads, step.head_dim, step.block_size, step.num_blocks
+    if step.num_pairs:
+        oracle.copy_blocks(kc, vc, step.cow_pairs.cpu().numpy(), num_kv_heads=hkv, head_dim=d,
+                           block_size=bs, num_blocks=N)
+    oracle.reshape_and_cache(W.host_array(step.new_key), W.host_array(step.new_value), kc, vc,
+                             step.slot_mapping.cpu().numpy(), num_kv_heads=hkv, head_dim=d,
+                             block_size=bs, num_blocks=N)
+    pools_ok = (W.host_array(step.key_cache).tobytes() == kc.tobytes() and
+                W.host_array(step.value_cache).tobytes() == vc.tobytes())
+    ref = oracle.paged_attention(W.host_array(step.query), kc, vc, step.block_tables.cpu().numpy(),
+                                 step.context_lens.cpu().numpy(), num_kv_heads=hkv, head_dim=d,
+                                 block_size=bs, scale=step.scale, num_blocks=N,
+                                 threads=max(1, min(16, os.cpu_count() or 1)))
+    got = step.out.double().cpu().numpy()
+    dtype = "bf16" if step.query.dtype == torch.bfloat16 else "fp32"
+    diff = np.abs(got - ref)
+    # A bf16 output is the fp32 result rounded to nearest even: it may also
+    # differ by half a bf16 ulp, at most 2^-8 |ref|.
+    bound = TOL[dtype] + (2.0 ** -8 * np.abs(ref) if step.out.dtype == torch.bfloat16 else 0.0)
+    ok = bool(np.all(diff <= bound)) and bool(np.isfinite(got).all())
+    return dict(max_abs_err=float(diff.max()) if diff.size else 0.0, tolerance=TOL[dtype],
+                rows=int(got.shape[0] * got.shape[1]), all_rows=True, pools_bit_exact=pools_ok,
+                passed=ok and pools_ok, seconds=round(time.perf_counter() - t0, 2))
+
+
+# ---- bandwidth ceilings -------------------------------------------------------
+
+def load_probe():
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_cache_305_amd", "libpaprobe.so")
+    if not os.path.exists(path):
+        raise SystemExit("libpaprobe.so is missing: build with python -m "
+                         "paged_kv_cache_305_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.probe_stream_read.argtypes = [vp, i64, vp, i32, i32, i32, vp]
+    lib.probe_block_gather.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, vp]
+    lib.probe_stream_read.restype = i32
+    lib.probe_block_gather.restype = i32
+    return lib
+
+
+def measure_ceilings(device, flush, reps=5):
+    """What the memory system delivers to the decode kernels' access
+    patterns on this GPU (libpaprobe.so), best over waves per CU {8, 16},
+    blocks in flight {2, 4} and normal / non-temporal loads:
+      stream: one 2 GiB buffer read once, in order;
+      gather: every 4 KiB block of a 2 GiB pool read once, in random order
+              (the paged K/V access pattern);
+      cache_gather: a 16 MiB pool read 64 times over in random order, so
+              that nearly all reads hit the caches (the shared-prefix
+              pattern: a few MB re-read by many waves)."""
+    import torch
+    lib = load_probe()
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    sink = torch.empty(cus * 16 * 64, dtype=torch.int32, device=device)
+    big = 2 << 30
+    buf = torch.ones(big // 8, dtype=torch.int64, device=device)
+    gen = torch.Generator(device=device).manual_seed(305)
+    ids_big = torch.randperm(big // 4096, generator=gen, device=device).to(torch.int32)
+    small_blocks = (16 << 20) // 4096
+    ids_small = torch.cat([torch.randperm(small_blocks, generator=gen, device=device)
+                           for _ in range(64)]).to(torch.int32)
+
+    def timed(launch):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps + 1)]
+        for a, b in evs:
+            if flush is not None:
+                flush.sum()
+            a.record()
+            rc = launch()
+            b.record()
+            if rc != 0:
+                raise RuntimeError("probe launch failed (%d)" % rc)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs[1:]])) / 1e3
+
+    best = {"stream": (0.0, None), "gather": (0.0, None), "cache_gather": (0.0, None)}
+    for wpc in (8, 16):
+        for depth in (2, 4):
+            for nt in (1, 0):
+                shape = dict(waves_per_cu=wpc, depth=depth, nontemporal=bool(nt))
+                w = cus * wpc
+                t = timed(lambda: lib.probe_stream_read(buf.data_ptr(), big, sink.data_ptr(), w,
+                                                        depth, nt, stream))
+                if big / t / 1e9 > best["stream"][0]:
+                    best["stream"] = (big / t / 1e9, shape)
+                t = timed(lambda: lib.probe_block_gather(buf.data_ptr(), big // 4096,
+                                                         ids_big.data_ptr(), ids_big.numel(),
+                                                         sink.data_ptr(), w, depth, nt, stream))
+                if big / t / 1e9 > best["gather"][0]:
+                    best["gather"] = (big / t / 1e9, shape)
+                n = ids_small.numel()
+                t = timed(lambda: lib.probe_block_gather(buf.data_ptr(), small_blocks,
+                                                         ids_small.data_ptr(), n,
+                                                         sink.data_ptr(), w, depth, nt, stream))
+                if n * 4096 / t / 1e9 > best["cache_gather"][0]:
+                    best["cache_gather"] = (n * 4096 / t / 1e9, shape)
+    del buf, ids_big, ids_small, sink
+    torch.cuda.empty_cache()
+    out = {k: dict(GBs=round(v[0], 1), frac_of_8TBs=round(v[0] / HBM_PEAK_GBS, 4), best=v[1])
+           for k, v in best.items()}
+    out["bytes"] = dict(stream=big, gather=big, cache_gather=64 * (16 << 20))
+    return out
+
+
+# ---- one workload -------------------------------------------------------------
+
+def measure_workload(name, args, device, flush, ceilings, parity=True):
+    """Time one workload's step (two passes of K steps after W warm-ups) and
+    check it against the oracle; returns (result dict, step, lens)."""
+    import torch
+    import paged_kv_cache_305_amd as pa
+    import workloads as W
+    log("%s: building the workload" % name)
+    step, lens, info = build_step(name, args.partition_size, device,
+                                  block_size=args.block_size if name == args.workload else None,
+                                  table_order=args.table_order, prefix=not args.no_prefix,
+                                  batch=args.batch if name == args.workload else None)
+    step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
+    step.cow_fused = {"auto": None, "fused": True, "separate": False}[args.cow]
+    torch.cuda.synchronize()
+    pools_before = None
+    if parity:
+        pools_before = (W.host_array(step.key_cache).copy(), W.host_array(step.value_cache).copy())
+    kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
+    if step.uses_fused_write:   # the launch also reads and stores each new token's K and V
+        attn_bytes += 2 * step.new_key.numel() * step.new_key.element_size() * 2 + \
+            step.slot_mapping.numel() * 8
+    if step.uses_fused_copy:    # ... and copies each pair's block, K and V (read + write)
+        block_bytes = step.num_kv_heads * step.block_size * step.head_dim * \
+            step.query.element_size()
+        attn_bytes += step.num_pairs * 2 * block_bytes * 2 + step.cow_src.numel() * 8
+    K, W_ = args.steps, args.warmup
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # torch creates the HIP event on first record; the library re-records it
+        return e
+    s_ev, e_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
+    ms_ev, me_ev, end_ev = [ev() for _ in range(K)], [ev() for _ in range(K)], \
+        [ev() for _ in range(K)]
+    torch.cuda.synchronize()
+    for _ in range(W_):
+        if flush is not None:
+            flush.sum()
+        step.run()
+    torch.cuda.synchronize()
+    # Two passes of K steps.  The first times the step as a caller runs it
+    # (value, ms_per_step).  The second brackets the main attention kernel
+    # with events the library records around its launch, and marks the end
+    # of the step (main kernel + merge): events inside the step add
+    # several microseconds of their own, so the first pass has none.
+    t0 = time.perf_counter()
+    for i in range(K):
+        if flush is not None:
+            flush.sum()
+        s_ev[i].record()
+        step.run()
+        e_ev[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(K):
+        if flush is not None:
+            flush.sum()
+        pa.set_timing_events(ms_ev[i], me_ev[i])
+        step.run()
+        end_ev[i].record()
+    torch.cuda.synchronize()
+    pa.set_timing_events(None, None)
+    step_ms = [s.elapsed_time(e) for s, e in zip(s_ev, e_ev)]
+    main_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, me_ev)]
+    attn_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, end_ev)]
+    t_step = float(np.mean(step_ms)) / 1e3
+    t_main = float(np.mean(main_ms)) / 1e3
+    t_attn = float(np.mean(attn_ms)) / 1e3
+    log("%s: step %.1f us (median %.1f), main kernel %.1f us, main + merge %.1f us" % (
+        name, t_step * 1e6, float(np.median(step_ms)) * 1e3, t_main * 1e6, t_attn * 1e6))
+
+    B = int(step.query.shape[0])
+    gbs = kv_bytes / t_step / 1e9
+    achieved = attn_bytes / t_main / 1e9
+    body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
+                          step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
+    kernel = "%s<%s>" % ("decode_prefix_tails" if step.prefix_len else
+                         "decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
+    default_variant = (name != args.workload or (
+        args.block_size in (None, W.CONFIGS.get(name, {}).get("block_size")) and
+        args.batch is None and args.table_order == "random")) and \
+        args.cache_write == "auto" and args.cow == "auto" and not args.no_prefix and \
+        not args.xcd_weights
+    gather = ceilings["gather"]["GBs"] if ceilings else None
+    roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                # The committed counters were taken on the workload as it
+                # stands (its own block size, batch and placement, default
+                # cache write and prefix use): any other variant gets none.
+                traffic=counter_traffic(name, args.partition_size) if default_variant else None,
+                algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
+                measured_ceiling_GBs=gather,
+                frac_of_measured_ceiling=round(achieved / gather, 4) if gather else None,
+                main_plus_merge_us=round(t_attn * 1e6, 2),
+                main_plus_merge_frac=round(attn_bytes / t_attn / 1e9 / HBM_PEAK_GBS, 4),
+                kernel_source_digest=kernel_source_digest())
+    result = {
+        "metric": "paged decode attention KV GB/s (fraction of HBM peak) and tokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(t_step * 1e3, 4),
+        "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[step.query.dtype],
+        "config": {"workload": WORKLOADS[name] + (
+                       " (batch set to %d)" % B if args.batch and name == args.workload else ""),
+                   "partition_size": args.partition_size,
+                   "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
+                   "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
+                   "shared_prefix_tokens": step.prefix_len,
+                   "cache_write": "inside the attention launch" if step.uses_fused_write
+                                  else "reshape_and_cache before the attention",
+                   "copy_on_write": "none" if not step.num_pairs else
+                                    "inside the attention launch" if step.uses_fused_copy
+                                    else "copy_blocks before the attention",
+                   "flush_between_steps": flush is not None, **info,
+                   **block_waste(step, lens)},
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B / t_step, 1),
+        "kv_tokens_per_s": round(float(lens.sum()) / t_step, 1),
+        # This step (cache write + attention) repeated for every layer of a
+        # model of this shape (32 layers for the 7B shape, 80 for the 70B
+        # shape), nothing else of the model: B / (t_step * layers).
+        **({"attn_only_model_tokens_per_s": round(B / (t_step * MODEL_LAYERS[name]), 1)}
+           if name in MODEL_LAYERS else {}),
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": roof,
+    }
+    if step.prefix_len and ceilings:
+        # The shared prompt's tiles are read once per block of 32 query rows
+        # (2 MFMA row tiles) of each KV head: cache-level reads of a few MB.
+        G = step.query.shape[1] // step.num_kv_heads
+        row_blocks = -(-(B * G) // 32)
+        per_token = step.num_kv_heads * step.head_dim * 2 * step.query.element_size()
+        pf_unique = step.prefix_len * per_token
+        cache_bytes = pf_unique * row_blocks
+        cg = ceilings["cache_gather"]["GBs"]
+        # The prefix's cache-level reads and the tails' HBM reads overlap
+        # in one launch: the launch takes at least the longer of the two
+        # at the measured ceilings.
+        t_hbm = (attn_bytes - pf_unique) / (gather * 1e9)
+        t_cache = cache_bytes / (cg * 1e9)
+        result["roofline_cache"] = dict(
+            bound="cache", kernel=kernel, prefix_unique_bytes=pf_unique,
+            prefix_reads_per_tile=row_blocks, cache_bytes_per_launch=cache_bytes,
+            achieved=round(cache_bytes / t_main / 1e9, 1), peak=cg, unit="GB/s",
+            peak_source="measured cache-level 4 KiB gather (libpaprobe.so)",
+            frac=round(cache_bytes / t_main / 1e9 / cg, 4),
+            bound_us=round(max(t_hbm, t_cache) * 1e6, 2),
+            frac_of_bound=round(max(t_hbm, t_cache) / t_main, 4))
+    if args.graph:
+        step.capture()
+        g_s, g_e = [ev() for _ in range(K)], [ev() for _ in range(K)]
+        torch.cuda.synchronize()
+        for _ in range(W_):
+            if flush is not None:
+                flush.sum()
+            step.replay()
+        for i in range(K):
+            if flush is not None:
+                flush.sum()
+            g_s[i].record()
+            step.replay()
+            g_e[i].record()
+        torch.cuda.synchronize()
+        g_ms = [a.elapsed_time(b) for a, b in zip(g_s, g_e)]
+        result["graph"] = {"ms_per_step": round(float(np.mean(g_ms)), 4),
+                           "step_ms_median": round(float(np.median(g_ms)), 4),
+                           "value_GBs": round(kv_bytes / (float(np.mean(g_ms)) / 1e3) / 1e9, 1)}
+        log("%s: graph replay: step %.1f us" % (name, float(np.mean(g_ms)) * 1e3))
+    if parity:
+        result["parity"] = step_parity(step, pools_before)
+        log("%s: parity %s, max abs err %.3g over %d rows, pools bit-exact %s" % (
+            name, "ok" if result["parity"]["passed"] else "FAILED",
+            result["parity"]["max_abs_err"], result["parity"]["rows"],
+            result["parity"]["pools_bit_exact"]))
+    return result, step, lens
 
 
 def swap_bench(args, device):
@@ -329,13 +650,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="70b", choices=sorted(WORKLOADS),
+                    help="the workload of the headline line (default: the 70B-shaped step)")
+    ap.add_argument("--extras", default="7b,long,long32,shared,tiny",
+                    help="other workloads timed in the same run and reported under "
+                         "\"workloads\" (comma-separated, or none)")
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="tokens per split-K partition; 0 = none, -1 = balanced split")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--batch", type=int, default=None,
-                    help="sequences in the step (default: the workload's); lengths keep the "
-                         "workload's distribution")
+                    help="sequences in the headline step (default: the workload's); lengths "
+                         "keep the workload's distribution")
     ap.add_argument("--cache-write", choices=["auto", "fused", "separate"], default="auto",
                     help="write the new tokens inside the attention launch (fused), with "
                          "reshape_and_cache before it (separate); auto = fused")
@@ -347,9 +672,13 @@ def main():
                     help="per-XCD tile shares of the balanced split, 8 comma-separated ints, or "
                          "two (even,odd) repeated over the 8 XCDs (default: the library's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the timed steps")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the bandwidth-ceiling probes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--block-size", type=int, default=None,
-                    help="block size of the workload (default: the workload's own)")
+                    help="block size of the headline workload (default: the workload's own)")
     ap.add_argument("--table-order", choices=["random", "identity"], default="random",
                     help="physical blocks in random order (paged) or consecutive (contiguous)")
     ap.add_argument("--no-prefix", action="store_true",
@@ -360,6 +689,8 @@ def main():
     ap.add_argument("--waste-report", action="store_true",
                     help="only print the allocator's KV waste per workload and block size "
                          "(host only)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the bandwidth ceilings (libpaprobe.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -372,7 +703,6 @@ def main():
 
     import torch
     import paged_kv_cache_305_amd as pa
-    import workloads as W
     if args.waste_report:
         for row in waste_report():
             print(json.dumps(row), flush=True)
@@ -393,152 +723,60 @@ def main():
         swap_bench(args, device)
         return
 
-    log("building workload %s" % args.workload)
-    step, lens, info = build_step(args.workload, args.partition_size, device,
-                                  block_size=args.block_size, table_order=args.table_order,
-                                  prefix=not args.no_prefix, batch=args.batch)
-    step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
-    step.cow_fused = {"auto": None, "fused": True, "separate": False}[args.cow]
-    torch.cuda.synchronize()
-    kv_bytes, attn_bytes = algorithmic_bytes(step, lens)
-    if step.uses_fused_write:   # the launch also reads and stores each new token's K and V
-        attn_bytes += 2 * step.new_key.numel() * step.new_key.element_size() * 2 + \
-            step.slot_mapping.numel() * 8
-    if step.uses_fused_copy:    # ... and copies each pair's block, K and V (read + write)
-        block_bytes = step.num_kv_heads * step.block_size * step.head_dim * \
-            step.query.element_size()
-        attn_bytes += step.num_pairs * 2 * block_bytes * 2 + step.cow_src.numel() * 8
     flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=device)
+    ceilings = None
+    if not args.no_ceiling or args.ceiling:
+        log("measuring the bandwidth ceilings")
+        ceilings = measure_ceilings(device, flush)
+        log("ceilings: stream %.0f GB/s, 4 KiB gather %.0f GB/s, cache-level gather %.0f GB/s" % (
+            ceilings["stream"]["GBs"], ceilings["gather"]["GBs"],
+            ceilings["cache_gather"]["GBs"]))
+        if args.ceiling:
+            print(json.dumps({"ceilings": ceilings}), flush=True)
+            return
+
+    result, step, lens = measure_workload(args.workload, args, device, flush, ceilings,
+                                          parity=not args.no_parity)
     K, W_ = args.steps, args.warmup
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()   # torch creates the HIP event on first record; the library re-records it
-        return e
-    s_ev, e_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
-    ms_ev, me_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
-    torch.cuda.synchronize()
-
-    log("warmup %d steps" % W_)
-    for _ in range(W_):
-        if flush is not None:
-            flush.sum()
-        step.run()
-    torch.cuda.synchronize()
-    # Two passes of K steps.  The first times the step as a caller runs it
-    # (value, ms_per_step).  The second brackets the main attention kernel
-    # with events the library records around its launch (roofline): events
-    # inside the step add several microseconds of their own, so the first
-    # pass has none.
-    log("timing %d steps" % K)
-    t0 = time.perf_counter()
-    for i in range(K):
-        if flush is not None:
-            flush.sum()
-        s_ev[i].record()
-        step.run()
-        e_ev[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log("timing the main kernel over %d more steps" % K)
-    for i in range(K):
-        if flush is not None:
-            flush.sum()
-        pa.set_timing_events(ms_ev[i], me_ev[i])
-        step.run()
-    torch.cuda.synchronize()
-    pa.set_timing_events(None, None)
-    step_ms = [s.elapsed_time(e) for s, e in zip(s_ev, e_ev)]
-    main_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, me_ev)]
-    t_step = float(np.mean(step_ms)) / 1e3
-    t_main = float(np.mean(main_ms)) / 1e3
-    log("step %.1f us (median %.1f), main kernel %.1f us" % (
-        t_step * 1e6, float(np.median(step_ms)) * 1e3, t_main * 1e6))
-
-    B = int(step.query.shape[0])
-    gbs = kv_bytes / t_step / 1e9
-    achieved = attn_bytes / t_main / 1e9
-    body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
-                          step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
-    kernel = "%s<%s>" % ("decode_prefix_tails" if step.prefix_len else
-                         "decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
-    roof = dict(bound="hbm", kernel=kernel, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                # The committed counters were taken on the workload as it
-                # stands (its own block size, batch and placement, default
-                # cache write and prefix use): any other variant gets none.
-                traffic=counter_traffic(args.workload, args.partition_size)
-                if args.block_size in (None, W.CONFIGS.get(args.workload, {}).get("block_size")) and args.batch is None
-                and args.table_order == "random" and args.cache_write == "auto"
-                and args.cow == "auto" and not args.no_prefix and not args.xcd_weights else None,
-                algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
-                kernel_source_digest=kernel_source_digest())
-    result = {
-        "metric": "paged decode attention KV GB/s (fraction of HBM peak) and tokens/s",
-        "value": round(gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W_,
-        "ms_per_step": round(t_step * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[step.query.dtype],
+    line = {
+        "metric": result.pop("metric"), "value": result.pop("value"), "unit": result.pop("unit"),
+        "n_gpus": 1, "steps": K, "warmup": W_, "ms_per_step": result.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": result.pop("dtype"),
         "data": "synthetic (seeded N(0,1) K/V/q, seeded lengths and block permutation)",
-        "config": {"workload": WORKLOADS[args.workload] + (
-                       " (batch set to %d)" % B if args.batch else ""),
-                   "partition_size": args.partition_size,
-                   "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
-                   "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
-                   "shared_prefix_tokens": step.prefix_len,
-                   "cache_write": "inside the attention launch" if step.uses_fused_write
-                                  else "reshape_and_cache before the attention",
-                   "copy_on_write": "none" if not step.num_pairs else
-                                    "inside the attention launch" if step.uses_fused_copy
-                                    else "copy_blocks before the attention",
-                   "flush_between_steps": flush is not None, **info,
-                   **block_waste(step, lens)},
-        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(B / t_step, 1),
-        "kv_tokens_per_s": round(float(lens.sum()) / t_step, 1),
-        # This step (cache write + attention) repeated for every layer of a
-        # model of this shape (32 layers for the 7B shape, 80 for the 70B
-        # shape), nothing else of the model: B / (t_step * layers).
-        **({"attn_only_model_tokens_per_s": round(B / (t_step * MODEL_LAYERS[args.workload]), 1)}
-           if args.workload in MODEL_LAYERS else {}),
-        "step_ms_median": round(float(np.median(step_ms)), 4),
-        "step_ms_min": round(float(np.min(step_ms)), 4),
-        "wall_s_timed_loop": round(wall, 4),
-        "roofline": roof,
+        **result,
     }
-    if args.graph:
-        step.capture()
-        g_s, g_e = [ev() for _ in range(K)], [ev() for _ in range(K)]
-        torch.cuda.synchronize()
-        for _ in range(W_):
-            if flush is not None:
-                flush.sum()
-            step.replay()
-        for i in range(K):
-            if flush is not None:
-                flush.sum()
-            g_s[i].record()
-            step.replay()
-            g_e[i].record()
-        torch.cuda.synchronize()
-        g_ms = [a.elapsed_time(b) for a, b in zip(g_s, g_e)]
-        result["graph"] = {"ms_per_step": round(float(np.mean(g_ms)), 4),
-                           "step_ms_median": round(float(np.median(g_ms)), 4),
-                           "value_GBs": round(kv_bytes / (float(np.mean(g_ms)) / 1e3) / 1e9, 1)}
-        log("graph replay: step %.1f us" % (float(np.mean(g_ms)) * 1e3))
+    if ceilings:
+        line["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ~%.0f s, then ~%.0f s on one thread" % (
             args.cpu_seconds, args.cpu_seconds / 3))
-        result["cpu_baseline"] = cpu_baseline(step, lens, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(step, lens, args.cpu_seconds)
         one = cpu_baseline(step, lens, args.cpu_seconds / 3, threads=1)
-        result["cpu_baseline"]["single_thread"] = {
+        line["cpu_baseline"]["single_thread"] = {
             k: one[k] for k in ("value", "unit", "tokens_per_s", "seconds", "sample")}
-    print(json.dumps(result), flush=True)
+    del step
+    torch.cuda.empty_cache()
+    extras = [] if args.extras in ("", "none") else [x for x in args.extras.split(",")
+                                                     if x and x != args.workload]
+    if extras:
+        line["workloads"] = {}
+    for name in extras:
+        if name not in WORKLOADS or name == "swap":
+            raise SystemExit("unknown extra workload %r" % name)
+        r, st, _ = measure_workload(name, args, device, flush, ceilings,
+                                    parity=not args.no_parity)
+        r.pop("metric")
+        line["workloads"][name] = r
+        del st
+        torch.cuda.empty_cache()
+    failed = [n for n, r in [(args.workload, line)] + list(line.get("workloads", {}).items())
+              if "parity" in r and not r["parity"]["passed"]]
+    line["parity_all_passed"] = None if args.no_parity else not failed
+    print(json.dumps(line), flush=True)
+    if failed:
+        log("parity FAILED for: %s" % ", ".join(failed))
+        sys.exit(1)
 
 
 if __name__ == "__main__":

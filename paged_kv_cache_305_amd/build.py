@@ -2,8 +2,10 @@
 
     python -m paged_kv_cache_305_amd.build
 
-Objects go to ``paged_kv_cache_305_amd/_build/``; the shared library lands
-next to this file.  Every call recompiles every source.
+Objects go to ``paged_kv_cache_305_amd/_build/``; the shared libraries land
+next to this file: ``libpagedattn.so`` (the decode library) and
+``libpaprobe.so`` (bandwidth-ceiling probes the benchmark loads, declared in
+``include/paprobe.h``).  Every call recompiles every source.
 """
 from __future__ import annotations
 
@@ -19,10 +21,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
+PROBE_LIB = os.path.join(HERE, "libpaprobe.so")
 ARCH = "gfx950"
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 
 SOURCES = ["pa_decode.hip", "pa_cache.hip", "pa_api.cpp", "pa_allocator.cpp", "pa_error.cpp"]
+PROBE_SOURCES = ["pa_probe.hip"]
 
 # Packed fp32 VALU ops are turned off for device code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
@@ -52,18 +56,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
