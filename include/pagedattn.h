@@ -218,12 +218,14 @@ size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q
                                                  int32_t max_context_len, int32_t prefix_len,
                                                  pa_dtype kv_dtype);
 
-/* Tracing hook: while set, every pa_paged_attention_decode(_append) call
- * records hipEvent_t `before_main` just before its main attention kernel and
- * `after_main` just after it, on the call's stream (the log-sum-exp merge
- * kernel, when launched, comes after `after_main`).  Pass NULL, NULL to
- * stop.  The events are caller-owned; the setting is process-wide and not
- * thread-safe.  Used to time the main kernel alone. */
+/* Tracing hook: while set, every pa_paged_attention_decode(_append,
+ * _prefix) call made from the calling thread records hipEvent_t
+ * `before_main` just before its main attention kernel and `after_main` just
+ * after it, on the call's stream (the log-sum-exp merge kernel, when
+ * launched, comes after `after_main`).  Pass NULL, NULL to stop.  The
+ * events are caller-owned; the setting belongs to the calling thread only
+ * (calls from other threads record nothing).  Used to time the main kernel
+ * alone. */
 pa_status pa_set_timing_events(void *before_main, void *after_main);
 
 /* Tile shares of the balanced split (partition_size < 0), one weight per XCD
@@ -232,7 +234,8 @@ pa_status pa_set_timing_events(void *before_main, void *after_main);
  * {115,100,115,100,115,100,115,100}: on MI355X, waves on even-numbered XCDs
  * stream 10-15% faster than waves on odd-numbered ones.  weights == NULL
  * restores the default; otherwise n must be 8 and each weight in [1, 1000].
- * Process-wide.  Weights move the piece boundaries, so outputs may change in
+ * Process-wide and thread-safe: each call uses one whole setting, the one
+ * current when it was made.  Weights move the piece boundaries, so outputs may change in
  * their last bits (within the attention tolerance); for fixed weights,
  * sizes and lengths every call gives the same bits. */
 pa_status pa_set_balance_weights(const int32_t *weights, int32_t n);

@@ -192,8 +192,11 @@ def key_cache_shape(num_blocks, num_kv_heads, head_dim, block_size, dtype):
 
 
 def value_cache_shape(num_blocks, num_kv_heads, head_dim, block_size):
-    """[num_blocks, Hkv, d, block_size]."""
-    return (num_blocks, num_kv_heads, head_dim, block_size)
+    """[num_blocks, Hkv, block_size / 16, d, 16]: each feature's tokens in
+    groups of 16, one group per 16-token tile (block_size a multiple of 16)."""
+    if block_size % 16:
+        raise ValueError("block_size must be a multiple of 16, got %d" % block_size)
+    return (num_blocks, num_kv_heads, block_size // 16, head_dim, 16)
 
 
 def allocate_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device="cuda"):

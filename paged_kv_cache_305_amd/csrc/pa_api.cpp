@@ -5,7 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <atomic>
+#include <mutex>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -51,8 +51,10 @@ bool device_addressable(const void *p) {
   return at.type == hipMemoryTypeHost && at.devicePointer == p;
 }
 
-void *g_ev_before_main = nullptr;
-void *g_ev_after_main = nullptr;
+// Tracing hook (pa_set_timing_events): per calling thread, so that a thread
+// that times its calls never adds events to another thread's.
+thread_local void *g_ev_before_main = nullptr;
+thread_local void *g_ev_after_main = nullptr;
 
 // Per-XCD tile shares of the balanced split.  Measured on MI355X: waves on
 // even-numbered XCDs finish a fixed share 10-15% sooner than waves on
@@ -60,7 +62,10 @@ void *g_ev_after_main = nullptr;
 // A sweep of the even weight over 100..130 on two GPUs put the best
 // decode time at 115 for both the 7B- and 70B-shaped batches.
 constexpr int32_t kDefaultXcdWeights[8] = {115, 100, 115, 100, 115, 100, 115, 100};
-std::atomic<int32_t> g_xcd_weights[8] = {115, 100, 115, 100, 115, 100, 115, 100};
+// Process-wide; a setting is replaced and read as a whole under the mutex,
+// so a call never mixes two settings.
+std::mutex g_weights_mutex;
+int32_t g_xcd_weights[8] = {115, 100, 115, 100, 115, 100, 115, 100};
 
 int32_t partitions_for(int32_t max_context_len, int32_t partition_size) {
   if (partition_size <= 0) return 1;
@@ -100,7 +105,8 @@ size_t partial_rows(int32_t num_seqs, const pa::HeadUnits &hu, int32_t max_conte
 namespace pa {
 
 void balance_weights(int32_t out[8]) {
-  for (int i = 0; i < 8; ++i) out[i] = g_xcd_weights[i].load(std::memory_order_relaxed);
+  std::lock_guard<std::mutex> lock(g_weights_mutex);
+  for (int i = 0; i < 8; ++i) out[i] = g_xcd_weights[i];
 }
 
 WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments, size_t waves,
@@ -144,7 +150,8 @@ extern "C" {
 pa_status pa_set_balance_weights(const int32_t *weights, int32_t n) {
   pa_clear_error();
   if (weights == nullptr) {
-    for (int i = 0; i < 8; ++i) g_xcd_weights[i].store(kDefaultXcdWeights[i]);
+    std::lock_guard<std::mutex> lock(g_weights_mutex);
+    for (int i = 0; i < 8; ++i) g_xcd_weights[i] = kDefaultXcdWeights[i];
     return PA_OK;
   }
   if (n != 8)
@@ -153,7 +160,8 @@ pa_status pa_set_balance_weights(const int32_t *weights, int32_t n) {
     if (weights[i] < 1 || weights[i] > 1000)
       return pa_fail(PA_ERR_INVALID_ARG, "pa_set_balance_weights: weight %d = %d outside [1, 1000]",
                      i, weights[i]);
-  for (int i = 0; i < 8; ++i) g_xcd_weights[i].store(weights[i]);
+  std::lock_guard<std::mutex> lock(g_weights_mutex);
+  for (int i = 0; i < 8; ++i) g_xcd_weights[i] = weights[i];
   return PA_OK;
 }
 
