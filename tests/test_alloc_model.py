@@ -16,7 +16,7 @@ import pytest
 from oracle.alloc_model import (AllocError, BlockAllocatorModel, ERR_INVALID_ARG,
                                 ERR_OUT_OF_BLOCKS, ERR_UNKNOWN_SEQ)
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shared_prompt_l138.json")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shared_prompt_worked_example.json")
 
 
 def _golden():

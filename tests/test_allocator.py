@@ -11,7 +11,7 @@ import paged_kv_cache_305_amd as pa
 from oracle.alloc_model import AllocError, BlockAllocatorModel
 from tests.test_alloc_model import random_trace
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shared_prompt_l138.json")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "shared_prompt_worked_example.json")
 
 
 def apply_cpp(a, op):
