@@ -178,6 +178,32 @@ pa_status pa_paged_attention_decode_append(
     pa_dtype out_dtype, uint32_t flags, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * paged_attention_decode_noalloc -- pa_paged_attention_decode_append with
+ * no workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Every argument, result and error is as in
+ * pa_paged_attention_decode_append, and new_key, new_value, slot_mapping
+ * and cow_src may all be NULL (the plain pa_paged_attention_decode).  The
+ * call's scratch (partial rows, merge counters, per-wave records) is a
+ * device array the library holds, 64 MiB on each GPU it runs on, kept until
+ * the process ends; the call allocates nothing.  Calls whose sizes need
+ * more scratch than that (as pa_paged_attention_workspace_bytes reports)
+ * return PA_ERR_INVALID_ARG before any launch; a 70B-shaped batch (256
+ * sequences, 64/8 heads, head_dim 128, 4096 tokens) needs about 43 MB.  The
+ * kernels reset what they count with, so the array needs no clearing, but
+ * calls on one GPU share it: calls that may overlap on one GPU (other
+ * streams) race and must not be made.
+ * ---------------------------------------------------------------------- */
+pa_status pa_paged_attention_decode_noalloc(
+    void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
+    const void *new_value, const int64_t *slot_mapping, const int64_t *cow_src,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype, uint32_t flags,
+    void *stream);
+
+/* ------------------------------------------------------------------------
  * paged_attention_decode_prefix -- the same attention when every sequence
  * starts with the same prefix_len tokens stored in the same physical blocks
  * (parallel samples or beam candidates of one prompt: inferensys glossary

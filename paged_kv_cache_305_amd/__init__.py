@@ -8,6 +8,8 @@ Python binding:
     per-sequence block tables (HIP kernels; MFMA for grouped-query heads);
   * ``paged_attention_decode_prefix`` -- the same with a prefix shared by
     every sequence read once for all of them;
+  * ``paged_attention_decode_noalloc`` -- the decode step with the
+    library's own device scratch instead of a workspace (allocates nothing);
   * ``reshape_and_cache`` -- write new tokens' K/V into their slots;
   * ``copy_blocks`` -- the copy of copy-on-write;
   * ``reshape_and_cache_layers``, ``copy_blocks_layers`` -- both over every
@@ -23,4 +25,5 @@ from ._binding import (  # noqa: F401
     allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
     paged_attention_workspace_bytes, reshape_and_cache, set_balance_weights, set_timing_events,
     swap_blocks, value_cache_shape, pointer_array, reshape_and_cache_layers, copy_blocks_layers,
-    paged_attention_decode_prefix, paged_attention_prefix_workspace_bytes)
+    paged_attention_decode_prefix, paged_attention_prefix_workspace_bytes,
+    paged_attention_decode_noalloc)

@@ -33,6 +33,7 @@ PA_DECODE_KV_REUSED = 1
 EXPORTS = (
     "pa_last_error", "pa_version",
     "pa_paged_attention_decode", "pa_paged_attention_decode_append",
+    "pa_paged_attention_decode_noalloc",
     "pa_paged_attention_decode_prefix", "pa_paged_attention_prefix_workspace_bytes",
     "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
     "pa_set_balance_weights",
@@ -68,6 +69,9 @@ def _declare(lib):
         "pa_paged_attention_decode_append": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
+        "pa_paged_attention_decode_noalloc": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
+                                                    i32, ctypes.c_uint32, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
@@ -314,23 +318,11 @@ def paged_attention_decode_prefix(out, query, key_cache, value_cache, block_tabl
     return out
 
 
-def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, *,
-                           num_kv_heads: int, block_size: int, max_context_len: int,
-                           scale: float, partition_size: int = 0, workspace=None,
-                           num_blocks: Optional[int] = None, kv_reused: bool = False,
-                           new_key=None, new_value=None, slot_mapping=None, cow_src=None,
-                           stream=None):
-    """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables.
-
-    kv_reused: some physical blocks are read by several sequences (shared
-    prefixes): keep K/V in the caches instead of streaming them.
-
-    new_key, new_value ([B, Hkv, d]) and slot_mapping (int64 [B]), given
-    together: each sequence's last position is this new token, written into
-    its slot by the same launch (pa_paged_attention_decode_append).
-    cow_src (int64 [B], optional with them): the copy-on-write source of
-    each sequence's new-token block, copied inside the launch (-1: none)."""
-    lib = load()
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, num_kv_heads,
+                 block_size, max_context_len, scale, partition_size, num_blocks, kv_reused,
+                 new_key, new_value, slot_mapping, cow_src):
+    """Checked pointers and sizes of a decode call: (appending, new-token
+    pointers, arguments after them up to the flags)."""
     dev = query.device
     appending = new_key is not None or new_value is not None or slot_mapping is not None
     if cow_src is not None and not appending:
@@ -357,16 +349,43 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
         raise ValueError("pools hold fewer than num_blocks blocks")
     news = _new_token_ptrs(new_key, new_value, slot_mapping, B, num_kv_heads, d, query.dtype, dev,
                            cow_src)
-    need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
-                                           partition_size, query.dtype)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr, ws_bytes = (0, 0) if workspace is None else (
-        _dev(workspace, "workspace", dev).data_ptr(), workspace.numel() * workspace.element_size())
     tail = (block_tables.data_ptr(), context_lens.data_ptr(), B, hq, num_kv_heads, d, block_size,
             int(block_tables.shape[1]), nb, int(max_context_len), float(scale),
             int(partition_size), _dtype_code(query), _dtype_code(out),
-            PA_DECODE_KV_REUSED if kv_reused else 0, ws_ptr, ws_bytes, _stream(dev, stream))
+            PA_DECODE_KV_REUSED if kv_reused else 0)
+    return appending, news, tail
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, *,
+                           num_kv_heads: int, block_size: int, max_context_len: int,
+                           scale: float, partition_size: int = 0, workspace=None,
+                           num_blocks: Optional[int] = None, kv_reused: bool = False,
+                           new_key=None, new_value=None, slot_mapping=None, cow_src=None,
+                           stream=None):
+    """out[B, Hq, d] = softmax(scale q K^T) V per sequence, K/V read through the tables.
+
+    kv_reused: some physical blocks are read by several sequences (shared
+    prefixes): keep K/V in the caches instead of streaming them.
+
+    new_key, new_value ([B, Hkv, d]) and slot_mapping (int64 [B]), given
+    together: each sequence's last position is this new token, written into
+    its slot by the same launch (pa_paged_attention_decode_append).
+    cow_src (int64 [B], optional with them): the copy-on-write source of
+    each sequence's new-token block, copied inside the launch (-1: none)."""
+    lib = load()
+    dev = query.device
+    appending, news, tail = _decode_args(out, query, key_cache, value_cache, block_tables,
+                                         context_lens, num_kv_heads, block_size, max_context_len,
+                                         scale, partition_size, num_blocks, kv_reused, new_key,
+                                         new_value, slot_mapping, cow_src)
+    B, hq, d = query.shape
+    need = paged_attention_workspace_bytes(B, hq, num_kv_heads, d, max_context_len,
+                                           partition_size, query.dtype)
+    if need and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=dev)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (
+        _dev(workspace, "workspace", dev).data_ptr(), workspace.numel() * workspace.element_size())
+    tail = tail + (ws_ptr, ws_bytes, _stream(dev, stream))
     if appending:
         _check(lib.pa_paged_attention_decode_append(
             out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
@@ -375,6 +394,27 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
         _check(lib.pa_paged_attention_decode(
             out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
             *tail))
+    return out
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, *, num_kv_heads: int, block_size: int,
+                                   max_context_len: int, scale: float, partition_size: int = 0,
+                                   num_blocks: Optional[int] = None, kv_reused: bool = False,
+                                   new_key=None, new_value=None, slot_mapping=None, cow_src=None,
+                                   stream=None):
+    """paged_attention_decode without a workspace: the library's own device
+    array holds the call's scratch, so nothing is allocated (callers that
+    cannot allocate, e.g. under graph capture).  Calls that would need more
+    scratch than the array holds raise PagedAttnError; calls that overlap on
+    one GPU race."""
+    lib = load()
+    _, news, tail = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                                 num_kv_heads, block_size, max_context_len, scale, partition_size,
+                                 num_blocks, kv_reused, new_key, new_value, slot_mapping, cow_src)
+    _check(lib.pa_paged_attention_decode_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), *news,
+        *tail, _stream(query.device, stream)))
     return out
 
 

@@ -207,7 +207,7 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                       float scale, int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype,
                       uint32_t flags, void *workspace, size_t workspace_bytes, void *stream,
-                      int32_t prefix_len = 0) {
+                      int32_t prefix_len = 0, bool own_scratch = false) {
   const bool appending = new_key != nullptr || new_value != nullptr || slot_mapping != nullptr;
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -268,6 +268,16 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
       partial_rows(num_seqs, hu, max_context_len, partition_size, bound), head_dim,
       partition_size < 0 ? (size_t)num_seqs * hu.units : 0,
       partition_size < 0 ? (size_t)bound : 0, pf.partial_rows);
+  if (own_scratch && ws.total > 0) {
+    // The library's device array stands in for the caller's workspace.
+    if (ws.total > pa::kNoAllocScratchBytes)
+      return pa_fail(PA_ERR_INVALID_ARG, "%s: these sizes need %zu bytes of scratch; the "
+                     "library's array holds %zu (use pa_paged_attention_decode_append with a "
+                     "workspace)", fn, ws.total, pa::kNoAllocScratchBytes);
+    const int e = pa::noalloc_scratch(&workspace);
+    if (e != 0) return hip_fail(fn, e);
+    workspace_bytes = pa::kNoAllocScratchBytes;
+  }
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return pa_fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes needed, got %zu", fn,
@@ -470,6 +480,22 @@ pa_status pa_paged_attention_decode_append(
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, partition_size, kv_dtype, out_dtype,
                      flags, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_paged_attention_decode_noalloc(
+    void *out, const void *query, void *key_cache, void *value_cache, const void *new_key,
+    const void *new_value, const int64_t *slot_mapping, const int64_t *cow_src,
+    const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+    int32_t partition_size, pa_dtype kv_dtype, pa_dtype out_dtype, uint32_t flags,
+    void *stream) {
+  pa_clear_error();
+  return decode_call("pa_paged_attention_decode_noalloc", out, query, key_cache, value_cache,
+                     new_key, new_value, slot_mapping, cow_src, block_tables, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                     kv_dtype, out_dtype, flags, nullptr, 0, stream, 0, true);
 }
 
 pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,

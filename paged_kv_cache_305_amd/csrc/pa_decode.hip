@@ -53,10 +53,20 @@
 // exponentiated with v_exp_f32; the stored partition maxima are base-2.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pa_internal.h"
 #include "pa_launch_map.h"
+
+// Scratch of pa_paged_attention_decode_noalloc, for callers that cannot
+// allocate device memory: the call's partial rows, merge counters and
+// per-wave records live here instead of in a caller's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses this name as an address (on the host it is only a stand-in
+// for the symbol): noalloc_scratch() looks the device address up.  Calls on
+// one GPU share the array, so calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[pa::kNoAllocScratchBytes];
 
 namespace pa {
 namespace {
@@ -1853,6 +1863,27 @@ hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
 }
 
 }  // namespace
+
+int noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex m;
+  static void *per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(m);
+  if (per_device[dev] == nullptr) {
+    // Once per device, with that device current: its copy of the array.
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return (int)hipSuccess;
+}
 
 BalancedPlan balanced_plan(const DecodeArgs &a, int units, int resident) {
   // Reused blocks: split by XCD so that each KV head's blocks stay in one

@@ -91,6 +91,15 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(size_t rows, int32_t head_dim, size_t segments,
                                  size_t waves, size_t prefix_rows = 0);
 
+// The library's own device scratch for pa_paged_attention_decode_noalloc:
+// a file-scope device array of this many bytes in pa_decode.hip, one copy
+// per GPU, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept; returns
+// hipError_t as int.
+int noalloc_scratch(void **ptr);
+
 // Kernel launchers (pa_decode.hip, pa_cache.hip); they return hipError_t as int.
 int launch_decode(const DecodeArgs &a, void *stream);
 int launch_reshape_and_cache(const void *key, const void *value, void *key_cache,

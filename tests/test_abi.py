@@ -181,3 +181,14 @@ def test_balance_weights_are_validated():
     with pytest.raises(pa.PagedAttnError):
         pa.set_balance_weights([100] * 7 + [1001])
     pa.set_balance_weights(None)
+
+
+def test_noalloc_refuses_more_scratch_than_its_array_on_the_host():
+    """The no-workspace call checks its sizes against the library's 64 MiB
+    device array before touching any device: a fixed split of 8 sequences
+    into 2048 partitions of 64/8 heads needs 545 MB of partial rows."""
+    lib = pa.load()
+    args = (16, 32, 48, 64, NULL, NULL, NULL, NULL, 8, 8, 8, 64, 8, 128, 16, 2048, 1 << 20,
+            2048 * 16, 0.1, 16, pa.PA_BF16, pa.PA_BF16, 0, NULL)
+    assert lib.pa_paged_attention_decode_noalloc(*args) == pa.PA_ERR_INVALID_ARG
+    assert b"scratch" in lib.pa_last_error()
