@@ -61,6 +61,8 @@ WORKLOADS = {
              "Bs 16, 255 x L~U[128,4096] + one L=131072",
     "swap": "preemption swap of the 7B-shaped step's blocks: GPU pool <-> pinned host pool "
             "(swap_blocks), both directions",
+    "cacheops": "the cache kernels on their own: reshape_and_cache of the 7B- and 70B-shaped "
+                "steps' new tokens, copy_blocks of the shared-prefix step's copy-on-write pairs",
 }
 HOST_LINK_PEAK_GBS = 64.0   # PCIe Gen5 x16, one direction
 
@@ -430,8 +432,8 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
         e.record()   # torch creates the HIP event on first record; the library re-records it
         return e
     s_ev, e_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
-    ms_ev, me_ev, end_ev = [ev() for _ in range(K)], [ev() for _ in range(K)], \
-        [ev() for _ in range(K)]
+    ms_ev, me_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
+    gs_ev, ge_ev = [ev() for _ in range(K)], [ev() for _ in range(K)]
     torch.cuda.synchronize()
     for _ in range(W_):
         if flush is not None:
@@ -439,10 +441,12 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
         step.run()
     torch.cuda.synchronize()
     # Two passes of K steps.  The first times the step as a caller runs it
-    # (value, ms_per_step).  The second brackets the main attention kernel
-    # with events the library records around its launch, and marks the end
-    # of the step (main kernel + merge): events inside the step add
-    # several microseconds of their own, so the first pass has none.
+    # (value, ms_per_step).  The second has the runtime stamp events with
+    # the main kernel's and the merge kernel's own start and end
+    # (pa_set_timing_events): their durations.  Events attached to a launch
+    # delay the next launch by several microseconds on ROCm, while in a step
+    # without events the merge starts as the main kernel ends (kernel
+    # traces), so main + merge is the sum of the two durations.
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
@@ -452,17 +456,20 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
         e_ev[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # A step merges unless every sequence fits one fixed partition.
+    merges = args.partition_size < 0 or (
+        args.partition_size > 0 and step.max_context_len > args.partition_size)
     for i in range(K):
         if flush is not None:
             flush.sum()
-        pa.set_timing_events(ms_ev[i], me_ev[i])
+        pa.set_timing_events(ms_ev[i], me_ev[i], *((gs_ev[i], ge_ev[i]) if merges else ()))
         step.run()
-        end_ev[i].record()
     torch.cuda.synchronize()
-    pa.set_timing_events(None, None)
+    pa.set_timing_events()
     step_ms = [s.elapsed_time(e) for s, e in zip(s_ev, e_ev)]
     main_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, me_ev)]
-    attn_ms = [s.elapsed_time(e) for s, e in zip(ms_ev, end_ev)]
+    merge_ms = [s.elapsed_time(e) for s, e in zip(gs_ev, ge_ev)] if merges else [0.0] * K
+    attn_ms = [a + b for a, b in zip(main_ms, merge_ms)]
     t_step = float(np.mean(step_ms)) / 1e3
     t_main = float(np.mean(main_ms)) / 1e3
     t_attn = float(np.mean(attn_ms)) / 1e3
@@ -491,6 +498,7 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
                 measured_ceiling_GBs=gather,
                 frac_of_measured_ceiling=round(achieved / gather, 4) if gather else None,
+                merge_us=round(float(np.mean(merge_ms)) * 1e3, 2),
                 main_plus_merge_us=round(t_attn * 1e6, 2),
                 main_plus_merge_frac=round(attn_bytes / t_attn / 1e9 / HBM_PEAK_GBS, 4),
                 kernel_source_digest=kernel_source_digest())
@@ -632,6 +640,100 @@ def swap_bench(args, device):
     print(json.dumps(result), flush=True)
 
 
+def cache_ops_bench(args, device, flush):
+    """reshape_and_cache and copy_blocks launched on their own, each timed
+    over K launches after W warm-ups (caches flushed before each), and
+    checked bit for bit against the oracle's scatter and copy on the whole
+    pools.  Algorithmic bytes: the payload read once and written once (plus
+    the slots or pairs)."""
+    import torch
+    import oracle
+    import paged_kv_cache_305_amd as pa
+    import workloads as W
+    from paged_kv_cache_305_amd.step import shared_prefix_step
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            if flush is not None:
+                flush.sum()
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            if flush is not None:
+                flush.sum()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+
+    def entry(kernel, t, alg, payload, ok, **extra):
+        return dict(kernel=kernel, avg_launch_us=round(t * 1e6, 2), payload_bytes=payload,
+                    algorithmic_bytes_per_launch=alg,
+                    roofline=dict(bound="hbm", achieved=round(alg / t / 1e9, 1),
+                                  peak=HBM_PEAK_GBS, unit="GB/s",
+                                  frac=round(alg / t / 1e9 / HBM_PEAK_GBS, 4)),
+                    pools_bit_exact=ok, **extra)
+
+    out = {}
+    for name in ("7b", "70b"):
+        case = W.make_case(name, device=device)
+        kc0, vc0 = W.host_array(case.key_cache).copy(), W.host_array(case.value_cache).copy()
+        slots = torch.as_tensor(case.slot_mapping).to(device)
+        fn = lambda: pa.reshape_and_cache(case.new_key, case.new_value, case.key_cache,
+                                          case.value_cache, slots, block_size=case.block_size,
+                                          num_blocks=case.num_blocks)
+        t = timed(fn)
+        oracle.reshape_and_cache(W.host_array(case.new_key), W.host_array(case.new_value), kc0,
+                                 vc0, case.slot_mapping, num_kv_heads=case.num_kv_heads,
+                                 head_dim=case.head_dim, block_size=case.block_size,
+                                 num_blocks=case.num_blocks)
+        ok = (W.host_array(case.key_cache).tobytes() == kc0.tobytes() and
+              W.host_array(case.value_cache).tobytes() == vc0.tobytes())
+        payload = 2 * case.new_key.numel() * case.new_key.element_size()
+        out["reshape_and_cache_" + name] = entry(
+            "reshape_and_cache_kernel", t, 2 * payload + 8 * case.batch, payload, ok,
+            tokens=case.batch, kv_heads=case.num_kv_heads)
+        log("reshape_and_cache (%s): %.2f us, pools bit-exact %s" % (name, t * 1e6, ok))
+        del case
+        torch.cuda.empty_cache()
+    plan = W.shared_plan()
+    tens = W.shared_tensors(plan, device=device)
+    step, rec = shared_prefix_step(plan, tens, partition_size=-1)
+    kc0, vc0 = W.host_array(step.key_cache).copy(), W.host_array(step.value_cache).copy()
+    fn = lambda: pa.copy_blocks(step.key_cache, step.value_cache, step.cow_pairs,
+                                num_kv_heads=step.num_kv_heads, head_dim=step.head_dim,
+                                block_size=step.block_size, num_blocks=step.num_blocks)
+    t = timed(fn)
+    oracle.copy_blocks(kc0, vc0, rec["pairs"], num_kv_heads=step.num_kv_heads,
+                       head_dim=step.head_dim, block_size=step.block_size,
+                       num_blocks=step.num_blocks)
+    ok = (W.host_array(step.key_cache).tobytes() == kc0.tobytes() and
+          W.host_array(step.value_cache).tobytes() == vc0.tobytes())
+    block = step.num_kv_heads * step.block_size * step.head_dim * step.query.element_size()
+    payload = 2 * step.num_pairs * block
+    out["copy_blocks_shared"] = entry("copy_blocks_kernel", t, 2 * payload + 16 * step.num_pairs,
+                                      payload, ok, pairs=step.num_pairs)
+    log("copy_blocks (%d pairs): %.2f us, pools bit-exact %s" % (step.num_pairs, t * 1e6, ok))
+    first = out["reshape_and_cache_7b"]
+    result = {
+        "metric": "cache kernels: GB/s of payload read + written (reshape_and_cache, copy_blocks)",
+        "value": first["roofline"]["achieved"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(first["avg_launch_us"] / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the workloads' seeded pools, new tokens and copy pairs)",
+        "config": {"workload": WORKLOADS["cacheops"]},
+        "roofline": dict(first["roofline"], traffic=None), "kernels": out,
+        "parity_all_passed": all(v["pools_bit_exact"] for v in out.values()),
+    }
+    print(json.dumps(result), flush=True)
+    if not result["parity_all_passed"]:
+        sys.exit(1)
+
+
 def copy_calibration(device, steps):
     """A plain 1 GiB device copy, for scaling the FETCH/WRITE counters."""
     import torch
@@ -724,6 +826,9 @@ def main():
         return
 
     flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=device)
+    if args.workload == "cacheops":
+        cache_ops_bench(args, device, flush)
+        return
     ceilings = None
     if not args.no_ceiling or args.ceiling:
         log("measuring the bandwidth ceilings")
@@ -762,7 +867,7 @@ def main():
     if extras:
         line["workloads"] = {}
     for name in extras:
-        if name not in WORKLOADS or name == "swap":
+        if name not in WORKLOADS or name in ("swap", "cacheops"):
             raise SystemExit("unknown extra workload %r" % name)
         r, st, _ = measure_workload(name, args, device, flush, ceilings,
                                     parity=not args.no_parity)

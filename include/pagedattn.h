@@ -245,14 +245,19 @@ size_t pa_paged_attention_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q
                                                  pa_dtype kv_dtype);
 
 /* Tracing hook: while set, every pa_paged_attention_decode(_append,
- * _prefix) call made from the calling thread records hipEvent_t
- * `before_main` just before its main attention kernel and `after_main` just
- * after it, on the call's stream (the log-sum-exp merge kernel, when
- * launched, comes after `after_main`).  Pass NULL, NULL to stop.  The
- * events are caller-owned; the setting belongs to the calling thread only
- * (calls from other threads record nothing).  Used to time the main kernel
- * alone. */
-pa_status pa_set_timing_events(void *before_main, void *after_main);
+ * _noalloc, _prefix) call made from the calling thread launches its main
+ * attention kernel with the hipEvent_t pair (main_start, main_end) and its
+ * log-sum-exp merge kernel, when it has one, with (merge_start,
+ * merge_end): the runtime stamps each pair with that kernel's own start and
+ * end time (hipExtLaunchKernel), so the elapsed time between a pair is
+ * that kernel's duration.  Any of the four may be NULL (not stamped); pass
+ * all NULL to stop.  On ROCm an end event delays the next launch on the
+ * stream by several microseconds, so the span from the main kernel's start
+ * to the merge kernel's end is best taken with only main_start and
+ * merge_end set.  The events are caller-owned; the setting belongs to the
+ * calling thread only (calls from other threads record nothing). */
+pa_status pa_set_timing_events(void *main_start, void *main_end, void *merge_start,
+                               void *merge_end);
 
 /* Tile shares of the balanced split (partition_size < 0), one weight per XCD
  * in workgroup dispatch order (workgroup w runs on XCD w mod 8): each wave's

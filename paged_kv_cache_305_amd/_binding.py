@@ -77,7 +77,7 @@ def _declare(lib):
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
         "pa_paged_attention_prefix_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
-        "pa_set_timing_events": (i32, [vp, vp]),
+        "pa_set_timing_events": (i32, [vp, vp, vp, vp]),
         "pa_set_balance_weights": (i32, [vp, i32]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
@@ -213,16 +213,19 @@ def allocate_pools(num_blocks, num_kv_heads, head_dim, block_size, dtype, device
     return k, v
 
 
-def set_timing_events(before_main=None, after_main=None):
-    """Record these torch.cuda.Events around the main attention kernel of every
-    later decode call (None, None stops)."""
+def set_timing_events(main_start=None, main_end=None, merge_start=None, merge_end=None):
+    """Stamp these torch.cuda.Events with the start and end of the main attention
+    kernel (and of the merge kernel) of every later decode call from this thread;
+    all None stops.  The runtime stamps them from the kernels themselves, so
+    main_start.elapsed_time(main_end) is the kernel's duration."""
     def h(e):
         if e is None:
             return None
         if not int(e.cuda_event):
             raise ValueError("record the event once first: torch creates HIP events lazily")
         return int(e.cuda_event)
-    _check(load().pa_set_timing_events(h(before_main), h(after_main)))
+    _check(load().pa_set_timing_events(h(main_start), h(main_end), h(merge_start),
+                                       h(merge_end)))
 
 
 def set_balance_weights(weights=None):

@@ -53,8 +53,8 @@ bool device_addressable(const void *p) {
 
 // Tracing hook (pa_set_timing_events): per calling thread, so that a thread
 // that times its calls never adds events to another thread's.
-thread_local void *g_ev_before_main = nullptr;
-thread_local void *g_ev_after_main = nullptr;
+thread_local void *g_ev_main[2] = {nullptr, nullptr};
+thread_local void *g_ev_merge[2] = {nullptr, nullptr};
 
 // Per-XCD tile shares of the balanced split.  Measured on MI355X: waves on
 // even-numbered XCDs finish a fixed share 10-15% sooner than waves on
@@ -165,12 +165,13 @@ pa_status pa_set_balance_weights(const int32_t *weights, int32_t n) {
   return PA_OK;
 }
 
-pa_status pa_set_timing_events(void *before_main, void *after_main) {
+pa_status pa_set_timing_events(void *main_start, void *main_end, void *merge_start,
+                               void *merge_end) {
   pa_clear_error();
-  if ((before_main == nullptr) != (after_main == nullptr))
-    return pa_fail(PA_ERR_INVALID_ARG, "pa_set_timing_events: set both events or neither");
-  g_ev_before_main = before_main;
-  g_ev_after_main = after_main;
+  g_ev_main[0] = main_start;
+  g_ev_main[1] = main_end;
+  g_ev_merge[0] = merge_start;
+  g_ev_merge[1] = merge_end;
   return PA_OK;
 }
 
@@ -399,8 +400,10 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
   a.pf_sum = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_sum_off) : nullptr;
   a.pf_acc = pf.partial_rows ? reinterpret_cast<float *>(wsb + ws.pf_acc_off) : nullptr;
   pa::balance_weights(a.xcd_weights);
-  a.ev_before_main = g_ev_before_main;
-  a.ev_after_main = g_ev_after_main;
+  a.ev_main_start = g_ev_main[0];
+  a.ev_main_end = g_ev_main[1];
+  a.ev_merge_start = g_ev_merge[0];
+  a.ev_merge_end = g_ev_merge[1];
   const int e = pa::launch_decode(a, stream);
   return e == 0 ? PA_OK : hip_fail(fn, e);
 }

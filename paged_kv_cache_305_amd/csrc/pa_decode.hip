@@ -51,6 +51,7 @@
 //
 // Softmax runs in base 2: logits are multiplied by scale * log2(e) and
 // exponentiated with v_exp_f32; the stored partition maxima are base-2.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -1693,6 +1694,18 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
 
 // ---- dispatch ----------------------------------------------------------------
 
+// Launch `kernel`(p).  With a pair of timing events (pa_set_timing_events)
+// the runtime stamps them with the kernel's own start and end, adding no
+// work to the stream; otherwise a plain launch.
+hipError_t launch(const void *kernel, dim3 grid, dim3 block, Params &p, hipStream_t st,
+                  void *ev_start = nullptr, void *ev_end = nullptr) {
+  void *args[] = {&p};
+  if (ev_start != nullptr || ev_end != nullptr)
+    return hipExtLaunchKernel(kernel, grid, block, args, 0, st, static_cast<hipEvent_t>(ev_start),
+                              static_cast<hipEvent_t>(ev_end), 0);
+  return hipLaunchKernel(kernel, grid, block, args, 0, st);
+}
+
 // Waves of `kernel` the device holds at once (64-thread workgroups).
 int resident_waves(const void *kernel) {
   int dev = 0, cus = 0, per_cu = 0;
@@ -1729,12 +1742,10 @@ hipError_t launch_balanced(const DecodeArgs &a, Params &p, hipStream_t st) {
     if (pf) {
       const int64_t grid = (int64_t)plan.waves + p.pf_waves;
       if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((decode_prefix_tails<Body>), dim3((unsigned)grid), dim3(64), 0, st, p);
-      return hipGetLastError();
+      return launch(k, dim3((unsigned)grid), dim3(64), p, st, a.ev_main_start, a.ev_main_end);
     }
   }
-  hipLaunchKernelGGL((decode_balanced<Body>), dim3(plan.waves), dim3(64), 0, st, p);
-  return hipGetLastError();
+  return launch(k, dim3(plan.waves), dim3(64), p, st, a.ev_main_start, a.ev_main_end);
 }
 
 template <class Body, typename OUT>
@@ -1744,9 +1755,9 @@ hipError_t launch_body(const DecodeArgs &a, Params &p, hipStream_t st) {
   } else {
     const int64_t grid = (int64_t)p.units * a.num_seqs * p.num_partitions;
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_fixed<Body>), dim3((unsigned)grid), dim3(64), 0, st, p);
+    return launch(reinterpret_cast<const void *>(&decode_fixed<Body>), dim3((unsigned)grid),
+                  dim3(64), p, st, a.ev_main_start, a.ev_main_end);
   }
-  return hipGetLastError();
 }
 
 template <typename OUT, bool NT>
@@ -1813,36 +1824,36 @@ int merge_waves(const DecodeArgs &a, const Params &p) {
 }
 
 template <int D, typename OUT>
-hipError_t launch_merge_d(const Params &p, int64_t rows, int nw, hipStream_t st) {
+hipError_t launch_merge_d(const DecodeArgs &a, Params &p, int64_t rows, int nw, hipStream_t st) {
+  const dim3 grid((unsigned)rows);
+  void *e0 = a.ev_merge_start, *e1 = a.ev_merge_end;
   if (nw == 4)
-    hipLaunchKernelGGL((decode_merge<D, OUT, 4>), dim3((unsigned)rows), dim3(256), 0, st, p);
-  else if (nw == 2)
-    hipLaunchKernelGGL((decode_merge<D, OUT, 2>), dim3((unsigned)rows), dim3(128), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_merge<D, OUT, 1>), dim3((unsigned)rows), dim3(64), 0, st, p);
-  return hipGetLastError();
+    return launch(reinterpret_cast<const void *>(&decode_merge<D, OUT, 4>), grid, dim3(256), p,
+                  st, e0, e1);
+  if (nw == 2)
+    return launch(reinterpret_cast<const void *>(&decode_merge<D, OUT, 2>), grid, dim3(128), p,
+                  st, e0, e1);
+  return launch(reinterpret_cast<const void *>(&decode_merge<D, OUT, 1>), grid, dim3(64), p, st,
+                e0, e1);
 }
 
 template <int D, typename OUT>
-hipError_t launch_merge_segments_d(const Params &p, int64_t segs, hipStream_t st) {
+hipError_t launch_merge_segments_d(const DecodeArgs &a, Params &p, int64_t segs,
+                                   hipStream_t st) {
   constexpr int RGN = 64 / (D / 4);
   const int rg = (p.gu + RGN - 1) / RGN;
   const int64_t n = segs > p.waves ? segs : p.waves;
   if (n > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n);
-  if (rg <= 1)
-    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 1>), grid, dim3(64), 0, st, p);
-  else if (rg <= 2)
-    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 2>), grid, dim3(64), 0, st, p);
-  else if (rg <= 4)
-    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 4>), grid, dim3(64), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_merge_segments<D, OUT, 8>), grid, dim3(64), 0, st, p);
-  return hipGetLastError();
+  const void *k = rg <= 1   ? reinterpret_cast<const void *>(&decode_merge_segments<D, OUT, 1>)
+                  : rg <= 2 ? reinterpret_cast<const void *>(&decode_merge_segments<D, OUT, 2>)
+                  : rg <= 4 ? reinterpret_cast<const void *>(&decode_merge_segments<D, OUT, 4>)
+                            : reinterpret_cast<const void *>(&decode_merge_segments<D, OUT, 8>);
+  return launch(k, grid, dim3(64), p, st, a.ev_merge_start, a.ev_merge_end);
 }
 
 template <typename OUT>
-hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
+hipError_t launch_merge(const DecodeArgs &a, Params &p, hipStream_t st) {
   const int64_t rows = (int64_t)a.num_seqs * p.units * p.gu;
   if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
   // Balanced split without a shared prefix, segments expected to span few
@@ -1854,12 +1865,12 @@ hipError_t launch_merge(const DecodeArgs &a, const Params &p, hipStream_t st) {
     const int64_t sx = (int64_t)a.num_seqs * (p.units / p.xsplit);
     const int64_t est = sx > 0 ? (p.waves / p.xsplit + sx - 1) / sx + 1 : 1;
     if (est <= kSegmentMergeMaxPieces) {
-      if (a.head_dim == 64) return launch_merge_segments_d<64, OUT>(p, segs, st);
-      return launch_merge_segments_d<128, OUT>(p, segs, st);
+      if (a.head_dim == 64) return launch_merge_segments_d<64, OUT>(a, p, segs, st);
+      return launch_merge_segments_d<128, OUT>(a, p, segs, st);
     }
   }
-  if (a.head_dim == 64) return launch_merge_d<64, OUT>(p, rows, merge_waves<64>(a, p), st);
-  return launch_merge_d<128, OUT>(p, rows, merge_waves<128>(a, p), st);
+  if (a.head_dim == 64) return launch_merge_d<64, OUT>(a, p, rows, merge_waves<64>(a, p), st);
+  return launch_merge_d<128, OUT>(a, p, rows, merge_waves<128>(a, p), st);
 }
 
 }  // namespace
@@ -1964,10 +1975,6 @@ int launch_decode(const DecodeArgs &a, void *stream) {
   p.pf_sum = a.pf_sum;
   p.pf_acc = a.pf_acc;
   hipError_t e;
-  if (a.ev_before_main) {
-    e = hipEventRecord(static_cast<hipEvent_t>(a.ev_before_main), st);
-    if (e != hipSuccess) return (int)e;
-  }
   if (a.prefix_len > 0) {
     e = plan_prefix(a, p);
     if (e != hipSuccess) return (int)e;
@@ -1982,10 +1989,6 @@ int launch_decode(const DecodeArgs &a, void *stream) {
     e = reused ? dispatch_out<float, false>(a, p, hu.mfma, st)
                : dispatch_out<float, true>(a, p, hu.mfma, st);
   if (e != hipSuccess) return (int)e;
-  if (a.ev_after_main) {
-    e = hipEventRecord(static_cast<hipEvent_t>(a.ev_after_main), st);
-    if (e != hipSuccess) return (int)e;
-  }
   const bool merge = a.partition_size < 0 || a.num_partitions > 1;
   if (!merge) return (int)hipSuccess;
   e = a.out_dtype == PA_BF16 ? launch_merge<bf16_t>(a, p, st) : launch_merge<float>(a, p, st);

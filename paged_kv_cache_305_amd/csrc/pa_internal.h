@@ -37,7 +37,9 @@ struct DecodeArgs {
   int32_t prefix_len;               // shared prefix tokens (0: none)
   float *pf_max, *pf_sum, *pf_acc;  // shared-prefix partials
   int32_t xcd_weights[8];           // balanced mode: relative tile share per XCD
-  void *ev_before_main, *ev_after_main;  // optional hipEvent_t pair around the main kernel
+  // Optional hipEvent_t pairs stamped with the main and merge kernels' own
+  // start and end (pa_set_timing_events); null: none.
+  void *ev_main_start, *ev_main_end, *ev_merge_start, *ev_merge_end;
 };
 
 // How query heads are grouped into head units (one wave's worth of heads).

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(pa.load()._name)
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_version() == 102
+    assert lib.pa_version() == 103
 
 
 NULL = None

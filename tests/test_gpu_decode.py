@@ -314,29 +314,33 @@ def test_deep_validation_rejects_bad_tables_without_launching(gpu, monkeypatch):
     assert torch.all(sentinel == 7.0)
 
 
-def test_timing_hook_brackets_the_main_kernel(gpu):
+def test_timing_hook_stamps_the_main_and_merge_kernels(gpu):
+    """The events get the kernels' own start and end: main and merge each
+    take a positive time, the merge starts after the main kernel ends, and
+    both lie inside events recorded around the whole step."""
     case = W.make_case("70b", device="cuda", batch=16, len_range=(500, 2000))
     from paged_kv_cache_305_amd.step import step_from_case
     step = step_from_case(case, partition_size=256)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for e in evs:
         e.record()
     torch.cuda.synchronize()
     with pytest.raises(ValueError):
         gpu.set_timing_events(torch.cuda.Event(enable_timing=True), evs[1])
-    gpu.set_timing_events(evs[1], evs[2])
+    gpu.set_timing_events(evs[1], evs[2], evs[3], evs[4])
     try:
         evs[0].record()
         step.run()
-        evs[3].record()
+        evs[5].record()
         torch.cuda.synchronize()
     finally:
-        gpu.set_timing_events(None, None)
-    main = evs[1].elapsed_time(evs[2])
-    whole = evs[0].elapsed_time(evs[3])
-    assert 0 < main <= whole
-    ref = oracle_decode(case, idx=[0, 5])
-    assert max_abs_err(step.out[[0, 5]], ref) <= TOL["bf16"]
+        gpu.set_timing_events()
+    main, merge = evs[1].elapsed_time(evs[2]), evs[3].elapsed_time(evs[4])
+    assert main > 0 and merge > 0
+    assert evs[2].elapsed_time(evs[3]) >= 0
+    assert evs[0].elapsed_time(evs[1]) >= 0 and evs[4].elapsed_time(evs[5]) >= 0
+    ref = oracle_decode(case)
+    assert max_abs_err(step.out, ref) <= TOL["bf16"]
 
 
 def test_balanced_results_do_not_depend_on_xcd_weights(gpu):
