@@ -193,14 +193,25 @@ constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
 constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16
 
-// Lane l gets the value of lane l ^ 16 (within each half-wave).
-__device__ __forceinline__ float xor16(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+// Max or sum of the values of lanes l and l ^ 16 (l ^ 32), in every lane:
+// v_permlane16_swap / v_permlane32_swap hand each lane both values of its
+// pair (lower lane first) without a trip through LDS.  Both orders of a
+// pair give the same bits (max and + are commutative).
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// Lane l gets the value of lane l ^ 32.
-__device__ __forceinline__ float xor32(float v) {
-  const int src = (lane_id() ^ 32) << 2;
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Max / sum over the 16 lanes of each row; every lane of the row gets it.
@@ -587,8 +598,7 @@ struct ValuBody {
     for (int j = 0; j < KJ; ++j)
 #pragma unroll
       for (int e = 0; e < X; ++e) dot = fmaf(q.v[j][e], elem<KV>(tl.k[j], e), dot);
-    dot += xor16(dot);
-    dot += xor32(dot);
+    dot = pair32_sum(pair16_sum(dot));
     const float sc = kt * 16 + t < pc.t1 ? dot : -INFINITY;
     const float mnew = fmaxf(a.m, row16_max(sc));
     const float alpha = fast_exp2(a.m - mnew);
@@ -785,8 +795,7 @@ struct MfmaBody {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = pos0 + r < pc.t1 ? s[r] * p.scale_log2e : -INFINITY;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair32_max(pair16_max(mx));
     const float mnew = fmaxf(a.m, mx);
     const float alpha = fast_exp2(a.m - mnew);
     a.m = mnew;
@@ -846,8 +855,7 @@ struct MfmaBody {
 
   __device__ static void finish(const Params &p, const Piece &pc, Acc &a) {
     const int g = lane_id() >> 4, hh = lane_id() & 15;
-    float ltot = a.lsum + xor16(a.lsum);
-    ltot += xor32(ltot);
+    const float ltot = pair32_sum(pair16_sum(a.lsum));
     const int h = group_head(p, pc.unit);
     if (h >= p.group) return;
     const int qh = (pc.unit / p.head_tiles) * p.group + h;
@@ -1268,8 +1276,7 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = sv[t][r] * p.scale_log2e;
       float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
+      mx = pair32_max(pair16_max(mx));
       const float mnew = fmaxf(acc[t].m, mx);
       const float alpha = fast_exp2(acc[t].m - mnew);
       acc[t].m = mnew;
@@ -1302,8 +1309,7 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
   }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    float ltot = acc[t].lsum + xor16(acc[t].lsum);
-    ltot += xor32(ltot);
+    const float ltot = pair32_sum(pair16_sum(acc[t].lsum));
     const int row = rb * 16 * RT + t * 16 + c;
     if (row >= R) continue;
     const int64_t pr = ((int64_t)chunk * p.num_kv_heads + h) * R + row;
