@@ -990,20 +990,32 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_fixed(Params p) 
   store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
 }
 
-// Sum over the wave (all lanes get it).
+// Sum over the wave (all lanes get it): within each row of 16 lanes by DPP,
+// then over the row pairs by lane-pair swaps; no LDS round trip.
 __device__ __forceinline__ int wave_sum(int v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += __builtin_amdgcn_mov_dpp(v, kQuadXor1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, kQuadXor2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, kRowHalfMirror, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, kRowMirror, 0xF, 0xF, false);
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = (int)(r16[0] + r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return (int)(r32[0] + r32[1]);
 }
 
-// Inclusive prefix sum over the wave's lanes.
+// Inclusive prefix sum over the wave's lanes: within each row of 16 lanes by
+// DPP row shifts (a lane shifted in from outside the row adds 0), then each
+// row adds the totals of the rows before it.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  return v;
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kRowShr8, 0xF, 0xF, false);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
 }
 
 // Extra tiles each nonempty segment counts for in the balanced split, placed
