@@ -1031,13 +1031,43 @@ constexpr int kSegmentCost = PA_SEGMENT_COST;
 // Extent of a segment of n real tiles on the balanced split's tile line.
 __device__ __forceinline__ int seg_extent(int n) { return n > 0 ? n + kSegmentCost : 0; }
 
-// Tiles of one unit summed over all sequences: sum_i ceil(L_i / 16).
-__device__ __forceinline__ int64_t tiles_per_unit(const Params &p) {
-  int64_t tot = 0;
-  for (int c = 0; c < p.num_seqs; c += 64) {
-    const int i = c + lane_id();
-    tot += wave_sum(i < p.num_seqs ? seg_extent(own_tiles(p, seq_len(p, i))) : 0);
+// The clamped context lengths a wave needs at set-up: the split's total and
+// its search both run over every sequence.  Up to 64 * kLenRegs sequences
+// are requested in one round of loads and kept in registers (lane l of
+// register r: sequence 64 r + l), so set-up waits on memory once instead of
+// once per 64 sequences for the total and again for the search.  Larger
+// batches read each 64-sequence chunk from memory when it is needed.
+constexpr int kLenRegs = 8;
+struct SetupLens {
+  int v[kLenRegs];
+  bool held;
+  __device__ __forceinline__ void load(const Params &p) {
+    held = p.num_seqs <= 64 * kLenRegs;
+    if (!held) return;
+#pragma unroll
+    for (int r = 0; r < kLenRegs; ++r) {
+      const int i = 64 * r + lane_id();
+      v[r] = i < p.num_seqs ? seq_len(p, i) : 0;
+    }
   }
+  // Length of sequence c + lane (0 past the last), c a multiple of 64.
+  __device__ __forceinline__ int chunk(const Params &p, int c) const {
+    if (held) {
+      const int r = c >> 6;
+      int x = 0;
+#pragma unroll
+      for (int k = 0; k < kLenRegs; ++k) x = r == k ? v[k] : x;
+      return x;
+    }
+    const int i = c + lane_id();
+    return i < p.num_seqs ? seq_len(p, i) : 0;
+  }
+};
+
+// Tiles of one unit summed over all sequences: sum_i ceil(L_i / 16).
+__device__ __forceinline__ int64_t tiles_per_unit(const Params &p, const SetupLens &sl) {
+  int64_t tot = 0;
+  for (int c = 0; c < p.num_seqs; c += 64) tot += wave_sum(seg_extent(own_tiles(p, sl.chunk(p, c))));
   return tot;
 }
 
@@ -1169,7 +1199,9 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   auto record = [&]() {
     if (p.wave_segs != nullptr && lane == 0) p.wave_segs[vb] = (int32_t)gen.first_g;
   };
-  const Split sp(p, tiles_per_unit(p));
+  SetupLens sl;
+  sl.load(p);
+  const Split sp(p, tiles_per_unit(p, sl));
   if (gen.unit >= sp.W) {
     record();
     return;
@@ -1181,8 +1213,7 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   gen.seq = -1;
   int64_t seq_first = 0, base = 0;
   for (int c = 0; c < p.num_seqs && gen.seq < 0; c += 64) {
-    const int i = c + lane;
-    const int n = i < p.num_seqs ? own_tiles(p, seq_len(p, i)) : 0;
+    const int n = own_tiles(p, sl.chunk(p, c));
     const int incl = wave_incl_scan(seg_extent(n));
     const uint64_t hit = __builtin_amdgcn_ballot_w64((base + incl) * gen.ux > gen.t);
     if (hit) {
@@ -1197,7 +1228,8 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
     record();
     return;
   }
-  gen.lens.load(p, gen.seq);
+  gen.lens.base = gen.seq & ~63;
+  gen.lens.vals = sl.chunk(p, gen.lens.base);
   gen.L = gen.lens.get(p, gen.seq);
   gen.k = (int)((gen.t - seq_first) / seg_extent(gen.n_seq));
   gen.a = (int)((gen.t - seq_first) % seg_extent(gen.n_seq));
@@ -1545,6 +1577,10 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
 // KB loads (no synchronisation), else max(4 KB, about sqrt(n)), so that the
 // leaders' folds and the last fold over the chunks take about as many
 // rounds.
+// Lambdas that hold references to register arrays must be inlined: an
+// outlined call would put those arrays in scratch memory.
+#define PA_INLINE_LAMBDA __attribute__((always_inline))
+
 template <int KB>
 __device__ __forceinline__ int merge_chunk(int n) {
   if (n <= 4 * KB) return n;
@@ -1567,7 +1603,7 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
   f32x4 ag[RG];
   // Fold `count` partial rows, ids first, first + step, ... (in that order),
   // for every row this lane group owns, into (mg, sg, ag).
-  auto fold = [&](int64_t first, int count, int step, int nh) {
+  auto fold = [&](int64_t first, int count, int step, int nh) PA_INLINE_LAMBDA {
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       mg[r] = -INFINITY;
@@ -1609,7 +1645,7 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
     }
   };
   // Segment g's first output row (query head), rows, output pointer.
-  auto rows_of = [&](int64_t g, int &nh) -> OUT * {
+  auto rows_of = [&](int64_t g, int &nh) PA_INLINE_LAMBDA -> OUT * {
     const int unit = (int)(g % p.units);
     int qh0;
     if (p.gu == 1) {   // VALU body: one query head per unit
@@ -1622,7 +1658,7 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
     }
     return static_cast<OUT *>(p.out) + ((g / p.units) * p.num_q_heads + qh0) * D + 4 * ch;
   };
-  auto store_rows = [&](OUT *out, int nh, bool zero) {
+  auto store_rows = [&](OUT *out, int nh, bool zero) PA_INLINE_LAMBDA {
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int hh = rg + RGN * r;
@@ -1634,7 +1670,7 @@ __global__ __launch_bounds__(64) void decode_merge_segments(Params p) {
     }
   };
   // Lead chunk c of segment g (owners u0..u1).
-  auto lead = [&](int64_t g, int u0, int u1, int c) {
+  auto lead = [&](int64_t g, int u0, int u1, int c) PA_INLINE_LAMBDA {
     const int n = u1 - u0 + 1;
     const int C = merge_chunk<KB>(n), nc = (n + C - 1) / C;
     const int unit = (int)(g % p.units), seq = (int)(g / p.units);
