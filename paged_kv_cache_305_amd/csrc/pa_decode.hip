@@ -909,48 +909,121 @@ struct OnePiece {
 // writes them.  With copy-on-write inside the launch, the (sequence, KV
 // head)'s part of the copy source block is first copied over the slot's
 // block, as copy_blocks copies it (the source is never written here, and
-// the slot's block is read by no wave: its reader reads the source).  No wave of the launch reads these bytes from memory (the
-// tile holding a new token is patched in registers), so the stores wait
+// the slot's block is read by no wave: its reader reads the source).  No
+// wave of the launch reads these bytes from memory (the tile holding a new
+// token is patched in registers), so the stores wait
 // until the wave has finished its pieces: stores issued between the reads
 // slow the reads of every wave.  Wave w of n stores the (sequence, KV head)
 // pairs j = n - 1 - w, j + n, ...: the last waves to start take the first
 // pairs, so a grid larger than the GPU stores from its last waves.
+//
+// The first of those pairs can be staged (TokenStash): its slot, copy source
+// and token are requested at the start of the wave and parked in LDS, so
+// the end of the wave waits on no global read before its stores.
 template <class Body>
-__device__ __forceinline__ void store_new_tokens(const Params &p, int64_t w, int64_t n) {
+struct TokenStash {
+  using KV = typename Body::KVT;
+  static constexpr int X = 16 / (int)sizeof(KV);
+  static constexpr int C = Body::kHeadDim / X;   // 16-byte chunks of one K (or V) row
+  static_assert(2 * C <= 64, "one wave holds the token's K and V chunks");
+  static constexpr int kLdsChunks = 2 * C + 1;   // K chunks, V chunks, (slot, source)
+
+  // The pair wave w of n stores first, or -1.
+  __device__ static int64_t first_pair(const Params &p, int64_t w, int64_t n) {
+    const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads, j = n - 1 - w;
+    return p.slots != nullptr && j >= 0 && j < pairs ? j : -1;
+  }
+
+  int64_t j, slot, src;
+  u32x4 chunk;   // lane c < C: K chunk c; C <= lane < 2C: V chunk lane - C
+
+  __device__ __forceinline__ void request(const Params &p, int64_t w, int64_t n) {
+    j = first_pair(p, w, n);
+    if (j < 0) return;
+    const int seq = (int)(j / p.num_kv_heads), lane = lane_id();
+    slot = p.slots[seq];
+    src = p.cow_src != nullptr ? p.cow_src[seq] : -1;
+    const KV *row = static_cast<const KV *>(lane < C ? p.new_key : p.new_value) + j * Body::kHeadDim;
+    if (lane < 2 * C) chunk = *reinterpret_cast<const u32x4 *>(row + (lane % C) * X);
+  }
+  // Once the loads have arrived (after the set-up lengths, requested later).
+  __device__ __forceinline__ void park(u32x4 *lds) const {
+    if (j < 0) return;
+    const int lane = lane_id();
+    if (lane < 2 * C) lds[lane] = chunk;
+    if (lane == 0) {
+      union {
+        int64_t s[2];
+        u32x4 v;
+      } u;
+      u.s[0] = slot;
+      u.s[1] = src;
+      lds[2 * C] = u.v;
+    }
+  }
+};
+
+// Store pair j's token: K chunks and V elements from kp / vp (global input
+// or the stash in LDS), after copying the copy source's part of the block
+// when there is one.
+template <class Body>
+__device__ __forceinline__ void store_token_pair(const Params &p, int64_t j, int64_t slot,
+                                                 int64_t src, const typename Body::KVT *kp,
+                                                 const typename Body::KVT *vp) {
   using KV = typename Body::KVT;
   constexpr int D = Body::kHeadDim, BS = Body::kBlockSize;
   constexpr int X = 16 / (int)sizeof(KV);
-  if (p.slots == nullptr) return;
   const int lane = lane_id();
-  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
-  for (int64_t j = n - 1 - w; j < pairs; j += n) {
-    const int seq = (int)(j / p.num_kv_heads);
-    const int64_t slot = p.slots[seq];
-    if (slot < 0 || slot >= p.num_blocks * BS) continue;
-    const int o = (int)(slot % BS);
-    const int64_t base = (slot / BS * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
-    const KV *nk = static_cast<const KV *>(p.new_key) + j * D;
-    const KV *nv = static_cast<const KV *>(p.new_value) + j * D;
-    const int64_t src = p.cow_src != nullptr ? p.cow_src[seq] : -1;
-    if (src >= 0 && src < p.num_blocks && src != slot / BS) {
-      const int64_t sbase = (src * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
-      const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.key_cache) + sbase);
-      const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.value_cache) + sbase);
-      u32x4 *kd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.key_cache) + base);
-      u32x4 *vd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.value_cache) + base);
-      for (int i = lane; i < D * BS / X; i += 64) {
-        const u32x4 a = ks[i], b = vs[i];
-        kd[i] = a;
-        vd[i] = b;
-      }
-      // The token's stores below overwrite part of these: let these land first.
-      __builtin_amdgcn_s_waitcnt(0);
+  if (slot < 0 || slot >= p.num_blocks * BS) return;
+  const int o = (int)(slot % BS);
+  const int64_t base = (slot / BS * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
+  if (src >= 0 && src < p.num_blocks && src != slot / BS) {
+    const int64_t sbase = (src * p.num_kv_heads + j % p.num_kv_heads) * (int64_t)D * BS;
+    const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.key_cache) + sbase);
+    const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const KV *>(p.value_cache) + sbase);
+    u32x4 *kd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.key_cache) + base);
+    u32x4 *vd = reinterpret_cast<u32x4 *>(reinterpret_cast<KV *>(p.value_cache) + base);
+    for (int i = lane; i < D * BS / X; i += 64) {
+      const u32x4 a = ks[i], b = vs[i];
+      kd[i] = a;
+      vd[i] = b;
     }
-    KV *kc = reinterpret_cast<KV *>(p.key_cache) + base + o * X;
-    KV *vc = reinterpret_cast<KV *>(p.value_cache) + base + (o / 16) * D * 16 + o % 16;
-    for (int c = lane; c < D / X; c += 64)   // key chunk c: x features of the token
-      *reinterpret_cast<u32x4 *>(kc + c * BS * X) = *reinterpret_cast<const u32x4 *>(nk + c * X);
-    for (int e = lane; e < D; e += 64) vc[e * 16] = nv[e];   // value row e of its group
+    // The token's stores below overwrite part of these: let these land first.
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  KV *kc = reinterpret_cast<KV *>(p.key_cache) + base + o * X;
+  KV *vc = reinterpret_cast<KV *>(p.value_cache) + base + (o / 16) * D * 16 + o % 16;
+  for (int c = lane; c < D / X; c += 64)   // key chunk c: x features of the token
+    *reinterpret_cast<u32x4 *>(kc + c * BS * X) = *reinterpret_cast<const u32x4 *>(kp + c * X);
+  for (int e = lane; e < D; e += 64) vc[e * 16] = vp[e];   // value row e of its group
+}
+
+// Wave w of n: its pairs j = n - 1 - w, + n, ...; with `stash`, the first
+// one from the TokenStash parked there.
+template <class Body>
+__device__ __forceinline__ void store_new_tokens(const Params &p, int64_t w, int64_t n,
+                                                 const u32x4 *stash = nullptr) {
+  using KV = typename Body::KVT;
+  constexpr int D = Body::kHeadDim;
+  if (p.slots == nullptr) return;
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  int64_t j = n - 1 - w;
+  if (stash != nullptr && TokenStash<Body>::first_pair(p, w, n) >= 0) {
+    constexpr int C = TokenStash<Body>::C;
+    union {
+      int64_t s[2];
+      u32x4 v;
+    } u;
+    u.v = stash[2 * C];
+    const KV *kp = reinterpret_cast<const KV *>(stash), *vp = reinterpret_cast<const KV *>(stash + C);
+    store_token_pair<Body>(p, j, u.s[0], u.s[1], kp, vp);
+    j += n;
+  }
+  for (; j < pairs; j += n) {
+    const int seq = (int)(j / p.num_kv_heads);
+    const int64_t src = p.cow_src != nullptr ? p.cow_src[seq] : -1;
+    store_token_pair<Body>(p, j, p.slots[seq], src, static_cast<const KV *>(p.new_key) + j * D,
+                           static_cast<const KV *>(p.new_value) + j * D);
   }
 }
 
@@ -1185,9 +1258,11 @@ struct RangePieces {
 
 // vb: the wave's index in the split (its workgroup id, or its place among
 // the tail waves of a shared-prefix launch; vb and the workgroup id agree
-// mod 8, so the wave runs on XCD vb mod 8).
+// mod 8, so the wave runs on XCD vb mod 8).  tok_lds: where the wave's
+// first new token is staged for store_new_tokens(p, vb, n_store, tok_lds).
 template <class Body>
-__device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16], int vb) {
+__device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][16], int vb,
+                                             u32x4 *tok_lds, int64_t n_store) {
   const int lane = lane_id();
   RangePieces gen;
   gen.p = &p;
@@ -1199,9 +1274,14 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
   auto record = [&]() {
     if (p.wave_segs != nullptr && lane == 0) p.wave_segs[vb] = (int32_t)gen.first_g;
   };
+  // The token is requested before the lengths: once the split has waited
+  // for those, it has arrived too (loads return in order).
+  TokenStash<Body> ts;
+  ts.request(p, vb, n_store);
   SetupLens sl;
   sl.load(p);
   const Split sp(p, tiles_per_unit(p, sl));
+  ts.park(tok_lds);
   if (gen.unit >= sp.W) {
     record();
     return;
@@ -1243,8 +1323,9 @@ __device__ __forceinline__ void run_balanced(const Params &p, float (&p_lds)[2][
 template <class Body>
 __global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_balanced(Params p) {
   __shared__ float p_lds[2][16];
-  run_balanced<Body>(p, p_lds, (int)blockIdx.x);
-  store_new_tokens<Body>(p, blockIdx.x, gridDim.x);
+  __shared__ u32x4 tok_lds[TokenStash<Body>::kLdsChunks];
+  run_balanced<Body>(p, p_lds, (int)blockIdx.x, tok_lds, gridDim.x);
+  store_new_tokens<Body>(p, blockIdx.x, gridDim.x, tok_lds);
 }
 
 // ---- shared prefix -------------------------------------------------------------
@@ -1377,11 +1458,12 @@ __device__ __forceinline__ void run_prefix(const Params &p, float (&p_lds)[2][16
 template <class Body>
 __global__ __launch_bounds__(64) PA_OCCUPANCY(Body) void decode_prefix_tails(Params p) {
   __shared__ float p_lds[2][16];
+  __shared__ u32x4 tok_lds[TokenStash<Body>::kLdsChunks];
   const MixedWave mw = mixed_wave((int)blockIdx.x, p.waves, p.pf_waves);
   if (mw.tail) {
     if (mw.index >= p.waves) return;   // only if the grid were larger than both kinds
-    run_balanced<Body>(p, p_lds, mw.index);
-    store_new_tokens<Body>(p, mw.index, p.waves);
+    run_balanced<Body>(p, p_lds, mw.index, tok_lds, p.waves);
+    store_new_tokens<Body>(p, mw.index, p.waves, tok_lds);
   } else {
     if (mw.index >= p.pf_waves) return;
     run_prefix<Body::kHeadDim, Body::kBlockSize>(p, p_lds, mw.index);
