@@ -411,6 +411,8 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
                                   block_size=args.block_size if name == args.workload else None,
                                   table_order=args.table_order, prefix=not args.no_prefix,
                                   batch=args.batch if name == args.workload else None)
+    # The split the library runs for this step (auto: whole segments for short contexts).
+    ps = pa.resolve_partition(args.partition_size, step.max_context_len)
     step.fused = {"auto": None, "fused": True, "separate": False}[args.cache_write]
     step.cow_fused = {"auto": None, "fused": True, "separate": False}[args.cow]
     torch.cuda.synchronize()
@@ -457,8 +459,7 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # A step merges unless every sequence fits one fixed partition.
-    merges = args.partition_size < 0 or (
-        args.partition_size > 0 and step.max_context_len > args.partition_size)
+    merges = ps < 0 or (ps > 0 and step.max_context_len > ps)
     for i in range(K):
         if flush is not None:
             flush.sum()
@@ -482,7 +483,7 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
     body = "MfmaBody" if (step.query.dtype == torch.bfloat16 and
                           step.query.shape[1] // step.num_kv_heads >= 2) else "ValuBody"
     kernel = "%s<%s>" % ("decode_prefix_tails" if step.prefix_len else
-                         "decode_balanced" if args.partition_size < 0 else "decode_fixed", body)
+                         "decode_balanced" if ps < 0 else "decode_fixed", body)
     default_variant = (name != args.workload or (
         args.block_size in (None, W.CONFIGS.get(name, {}).get("block_size")) and
         args.batch is None and args.table_order == "random")) and \
@@ -494,7 +495,7 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
                 # The committed counters were taken on the workload as it
                 # stands (its own block size, batch and placement, default
                 # cache write and prefix use): any other variant gets none.
-                traffic=counter_traffic(name, args.partition_size) if default_variant else None,
+                traffic=counter_traffic(name, ps) if default_variant else None,
                 algorithmic_bytes_per_launch=attn_bytes, avg_launch_us=round(t_main * 1e6, 2),
                 measured_ceiling_GBs=gather,
                 frac_of_measured_ceiling=round(achieved / gather, 4) if gather else None,
@@ -510,7 +511,7 @@ def measure_workload(name, args, device, flush, ceilings, parity=True):
         "dtype": {torch.bfloat16: "bf16", torch.float32: "fp32"}[step.query.dtype],
         "config": {"workload": WORKLOADS[name] + (
                        " (batch set to %d)" % B if args.batch and name == args.workload else ""),
-                   "partition_size": args.partition_size,
+                   "partition_size": args.partition_size, "partition_resolved": ps,
                    "batch": B, "kv_tokens": int(lens.sum()), "kv_bytes": kv_bytes,
                    "kv_loads": "cached (blocks reused)" if step.kv_reused else "streamed",
                    "shared_prefix_tokens": step.prefix_len,
@@ -757,8 +758,9 @@ def main():
     ap.add_argument("--extras", default="7b,long,long32,shared,tiny",
                     help="other workloads timed in the same run and reported under "
                          "\"workloads\" (comma-separated, or none)")
-    ap.add_argument("--partition-size", type=int, default=-1,
-                    help="tokens per split-K partition; 0 = none, -1 = balanced split")
+    ap.add_argument("--partition-size", type=int, default=-2,
+                    help="tokens per split-K partition; 0 = none, -1 = balanced split, "
+                         "-2 = auto (none up to 256 tokens of context, else balanced)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--batch", type=int, default=None,
                     help="sequences in the headline step (default: the workload's); lengths "

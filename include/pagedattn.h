@@ -60,6 +60,12 @@ typedef int32_t pa_dtype;
 
 /* partition_size of pa_paged_attention_decode: balanced split. */
 #define PA_PARTITION_BALANCED (-1)
+/* partition_size of pa_paged_attention_decode: one pass per (sequence, head)
+ * when max_context_len <= PA_AUTO_WHOLE_MAX_LEN, else the balanced split
+ * (pa_resolve_partition).  Below that length a single wave's chain is at most
+ * 16 tiles, and skipping the split skips its merge launch. */
+#define PA_PARTITION_AUTO (-2)
+#define PA_AUTO_WHOLE_MAX_LEN 256
 
 /* flags of pa_paged_attention_decode.
  * PA_DECODE_KV_REUSED: some physical blocks are read by more than one
@@ -104,9 +110,11 @@ int32_t pa_version(void);
  *                   > 0  a multiple of block_size: ceil(L_i / partition_size)
  *                        partitions of that many tokens;
  *                   0    no split, one pass per (sequence, head);
- *                   < 0  (PA_PARTITION_BALANCED) balanced: the tiles of all
- *                        sequences are cut into one range per wave the GPU
- *                        holds at once, sized per XCD by
+ *                   PA_PARTITION_AUTO (-2)  0 or balanced, by
+ *                        max_context_len (pa_resolve_partition);
+ *                   any other value < 0 (PA_PARTITION_BALANCED) balanced:
+ *                        the tiles of all sequences are cut into one range
+ *                        per wave the GPU holds at once, sized per XCD by
  *                        pa_set_balance_weights.
  *  flags          PA_DECODE_* bits (0: K/V streamed, each block read once).
  *  workspace      device scratch of at least
@@ -270,6 +278,12 @@ pa_status pa_set_timing_events(void *main_start, void *main_end, void *merge_sta
  * their last bits (within the attention tolerance); for fixed weights,
  * sizes and lengths every call gives the same bits. */
 pa_status pa_set_balance_weights(const int32_t *weights, int32_t n);
+
+/* The split a decode call with this partition_size and max_context_len
+ * runs: PA_PARTITION_AUTO gives 0 when max_context_len <=
+ * PA_AUTO_WHOLE_MAX_LEN and PA_PARTITION_BALANCED otherwise; any other value
+ * is returned as it is.  Host only, no device call. */
+int32_t pa_resolve_partition(int32_t partition_size, int32_t max_context_len);
 
 /* Bytes of workspace pa_paged_attention_decode (and _append) needs for these sizes on the
  * current device; 0 when every output row is written directly (no split).

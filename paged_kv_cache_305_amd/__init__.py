@@ -21,7 +21,8 @@ Python binding:
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARG, PA_ERR_OUT_OF_BLOCKS,
     PA_DECODE_KV_REUSED, PA_ERR_UNKNOWN_SEQ, PA_ERR_UNSUPPORTED, PA_FP32, PA_OK,
-    PA_PARTITION_BALANCED, BlockAllocator, PagedAttnError,
+    PA_PARTITION_AUTO, PA_PARTITION_BALANCED, PA_AUTO_WHOLE_MAX_LEN, BlockAllocator,
+    PagedAttnError, resolve_partition,
     allocate_pools, copy_blocks, key_cache_shape, load, paged_attention_decode,
     paged_attention_workspace_bytes, reshape_and_cache, set_balance_weights, set_timing_events,
     swap_blocks, value_cache_shape, pointer_array, reshape_and_cache_layers, copy_blocks_layers,

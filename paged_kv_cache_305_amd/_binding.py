@@ -27,6 +27,8 @@ PA_ERR_HIP = -5
 PA_FP32 = 0
 PA_BF16 = 1
 PA_PARTITION_BALANCED = -1
+PA_PARTITION_AUTO = -2
+PA_AUTO_WHOLE_MAX_LEN = 256
 PA_DECODE_KV_REUSED = 1
 
 # Every symbol include/pagedattn.h declares.
@@ -35,7 +37,7 @@ EXPORTS = (
     "pa_paged_attention_decode", "pa_paged_attention_decode_append",
     "pa_paged_attention_decode_noalloc",
     "pa_paged_attention_decode_prefix", "pa_paged_attention_prefix_workspace_bytes",
-    "pa_paged_attention_workspace_bytes", "pa_set_timing_events",
+    "pa_paged_attention_workspace_bytes", "pa_resolve_partition", "pa_set_timing_events",
     "pa_set_balance_weights",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks",
     "pa_reshape_and_cache_layers", "pa_copy_blocks_layers",
@@ -73,6 +75,7 @@ def _declare(lib):
                                                     i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                     i32, ctypes.c_uint32, vp]),
         "pa_paged_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "pa_resolve_partition": (i32, [i32, i32]),
         "pa_paged_attention_decode_prefix": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                    i32, i32, i32, i32, i64, i32, f32, i32, i32,
                                                    i32, ctypes.c_uint32, vp, sz, vp]),
@@ -236,6 +239,12 @@ def set_balance_weights(weights=None):
         return
     w = np.ascontiguousarray(np.asarray(weights, dtype=np.int32))
     _check(load().pa_set_balance_weights(w.ctypes.data, int(w.size)))
+
+
+def resolve_partition(partition_size: int, max_context_len: int) -> int:
+    """The split a decode call with these arguments runs (PA_PARTITION_AUTO
+    gives 0 or PA_PARTITION_BALANCED; other values are returned as they are)."""
+    return int(load().pa_resolve_partition(int(partition_size), int(max_context_len)))
 
 
 def paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

@@ -175,10 +175,16 @@ pa_status pa_set_timing_events(void *main_start, void *main_end, void *merge_sta
   return PA_OK;
 }
 
+int32_t pa_resolve_partition(int32_t partition_size, int32_t max_context_len) {
+  if (partition_size != PA_PARTITION_AUTO) return partition_size;
+  return max_context_len <= PA_AUTO_WHOLE_MAX_LEN ? 0 : PA_PARTITION_BALANCED;
+}
+
 size_t pa_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t max_context_len, int32_t partition_size,
                                           pa_dtype kv_dtype) {
+  partition_size = pa_resolve_partition(partition_size, max_context_len);
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_context_len < 0 ||
       elem_bytes(kv_dtype) == 0)
@@ -210,6 +216,7 @@ pa_status decode_call(const char *fn, void *out, const void *query, const void *
                       uint32_t flags, void *workspace, size_t workspace_bytes, void *stream,
                       int32_t prefix_len = 0, bool own_scratch = false) {
   const bool appending = new_key != nullptr || new_value != nullptr || slot_mapping != nullptr;
+  partition_size = pa_resolve_partition(partition_size, max_context_len);
   if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return pa_fail(PA_ERR_INVALID_ARG,

@@ -20,4 +20,4 @@ void pa_clear_error() { g_msg[0] = '\0'; }
 
 extern "C" const char *pa_last_error(void) { return g_msg; }
 
-extern "C" int32_t pa_version(void) { return 103; }
+extern "C" int32_t pa_version(void) { return 104; }

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(pa.load()._name)
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.pa_version() == 103
+    assert lib.pa_version() == 104
 
 
 NULL = None
@@ -151,6 +151,33 @@ def test_workspace_size():
     assert lib.pa_paged_attention_workspace_bytes(-1, 32, 8, 128, 10, 16, pa.PA_BF16) == 0
     assert lib.pa_paged_attention_workspace_bytes(4, 30, 8, 128, 10, 16, pa.PA_BF16) == 0
     assert lib.pa_paged_attention_workspace_bytes(4, 32, 8, 128, 10, 16, 9) == 0
+
+
+def header_define(name):
+    m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_partition_constants_are_the_headers():
+    assert header_define("PA_PARTITION_BALANCED") == pa.PA_PARTITION_BALANCED == -1
+    assert header_define("PA_PARTITION_AUTO") == pa.PA_PARTITION_AUTO == -2
+    assert header_define("PA_AUTO_WHOLE_MAX_LEN") == pa.PA_AUTO_WHOLE_MAX_LEN == 256
+
+
+def test_auto_partition_resolves_by_the_longest_context():
+    auto, bal = pa.PA_PARTITION_AUTO, pa.PA_PARTITION_BALANCED
+    limit = pa.PA_AUTO_WHOLE_MAX_LEN
+    assert pa.resolve_partition(auto, 0) == 0
+    assert pa.resolve_partition(auto, limit) == 0
+    assert pa.resolve_partition(auto, limit + 1) == bal
+    assert pa.resolve_partition(auto, 1 << 20) == bal
+    for ps in (bal, -7, 0, 16, 512):             # every other value is returned as it is
+        for mcl in (1, limit, 1 << 20):
+            assert pa.resolve_partition(ps, mcl) == ps
+    # The size query resolves the same way: whole segments need no workspace.
+    ws = pa.paged_attention_workspace_bytes
+    assert ws(64, 64, 8, 128, limit, auto, pa.PA_BF16) == 0
+    assert ws(64, 64, 8, 128, limit, 0, pa.PA_BF16) == 0
 
 
 def test_cache_calls_reject_bad_arguments():

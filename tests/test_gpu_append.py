@@ -93,7 +93,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("name,kw", CASES)
-@pytest.mark.parametrize("ps", [0, 16, 64, BAL])
+@pytest.mark.parametrize("ps", [0, 16, 64, BAL, -2])   # -2: PA_PARTITION_AUTO
 def test_append_equals_write_then_attend(gpu, name, kw, ps):
     case = W.make_case(name, device="cuda", **kw)
     if ps > 0 and ps % case.block_size:

@@ -111,6 +111,26 @@ def test_one_long_context_among_many_short_ones(gpu, kw):
         assert torch.equal(out, gpu_decode(gpu, case, partition_size=BAL, out_dtype=od))
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),                                               # fp32 MHA, L <= 100
+    ("70b", dict(batch=16, len_range=(0, 256))),                # MFMA body, empty rows
+    ("7b", dict(batch=8, len_range=(200, 256))),                # VALU body at the limit
+    ("70b", dict(batch=300, len_range=(1, 64))),                # more segments than waves
+    ("70b", dict(batch=4, len_range=(1, 600))),                 # longest > 256: balanced
+])
+def test_auto_partition_runs_the_split_it_resolves_to(gpu, name, kw):
+    """PA_PARTITION_AUTO runs whole segments when the longest context is at
+    most 256 tokens and the balanced split otherwise: its output equals that
+    split's bit for bit, and the oracle within tolerance."""
+    case = W.make_case(name, device="cuda", **kw)
+    mcl = int(case.context_lens.max())
+    want = gpu.resolve_partition(gpu.PA_PARTITION_AUTO, mcl)
+    assert want == (0 if mcl <= gpu.PA_AUTO_WHOLE_MAX_LEN else gpu.PA_PARTITION_BALANCED)
+    for od in (None, torch.float32):
+        out, _ = _check(gpu, case, gpu.PA_PARTITION_AUTO, out_dtype=od)
+        assert torch.equal(out, gpu_decode(gpu, case, partition_size=want, out_dtype=od))
+
+
 @pytest.mark.parametrize("name,kw", [("7b", dict(batch=3, len_range=(1, 300))),
                                      ("70b", dict(batch=3, len_range=(1, 300))),
                                      ("tiny", {})])
