@@ -1655,14 +1655,14 @@ __global__ __launch_bounds__(64 * NW) void decode_merge(Params p) {
 // hh = rg + RGN * r, r < RG, of the unit (one row with the VALU body).
 // Grid: max(segments, main-kernel waves).
 
-// Pieces per chunk of a segment of n pieces: one chunk up to four rounds of
-// KB loads (no synchronisation), else max(4 KB, about sqrt(n)), so that the
-// leaders' folds and the last fold over the chunks take about as many
-// rounds.
 // Lambdas that hold references to register arrays must be inlined: an
 // outlined call would put those arrays in scratch memory.
 #define PA_INLINE_LAMBDA __attribute__((always_inline))
 
+// Pieces per chunk of a segment of n pieces: one chunk up to four rounds of
+// KB loads (no synchronisation), else max(4 KB, about sqrt(n)), so that the
+// leaders' folds and the last fold over the chunks take about as many
+// rounds.
 template <int KB>
 __device__ __forceinline__ int merge_chunk(int n) {
   if (n <= 4 * KB) return n;
