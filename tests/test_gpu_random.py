@@ -1,6 +1,6 @@
 """Seeded random configurations across the parameter space, each checked
 against the oracle: K/V dtype, head_dim, block size, KV heads and group size,
-batch, lengths (empty and ragged sequences among them), split mode, output
+batch, lengths (empty and ragged sequences among them), split mode (auto too), output
 dtype, reused-block loads and the in-launch cache write.  Every case prints
 its configuration first, so a failure names it."""
 import numpy as np
@@ -29,7 +29,7 @@ def _config(k):
     lens[rng.random(batch) < 0.15] = 0
     if lens.max() == 0:
         lens[0] = 1
-    ps = int(rng.choice([-1, -1, 0, bs, 2 * bs, 512]))
+    ps = int(rng.choice([-1, -1, -2, 0, bs, 2 * bs, 512]))   # -2: PA_PARTITION_AUTO
     return dict(fp32=bool(rng.random() < 0.3), head_dim=int(rng.choice([64, 128])),
                 block_size=bs, num_kv_heads=hkv, num_q_heads=hkv * group,
                 lens=tuple(int(x) for x in lens), partition_size=ps,
