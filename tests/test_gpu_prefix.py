@@ -61,6 +61,9 @@ CASES = [
     ("7b", 3, (1000, 990, 1013, 1003), dict(num_q_heads=28, num_kv_heads=4)),   # G = 7
     # Fewer than 8 waves of each kind: no alternating runs at all.
     ("7b", 1, (3, 10), dict(num_q_heads=8, num_kv_heads=2)),
+    # A 16,000-token prefix in 12 chunks of 84 tiles: each prefix wave's
+    # table reads cross a 64-entry chunk.
+    ("70b", 1000, tuple(range(0, 320, 20)), dict(num_q_heads=128)),                # G = 16
 ]
 
 
