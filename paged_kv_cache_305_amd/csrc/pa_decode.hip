@@ -491,12 +491,19 @@ __device__ __forceinline__ void stream_pieces(const Params &p, Gen &gen, float (
   bool h0 = load_next(b0);
   bool h1 = load_next(b1);
   Body::ready_q(p, cp, qraw, q);   // after the first tiles are requested
+  // A wave that has just computed a tile issues the next tile's loads at a
+  // raised priority, ahead of the other wave's arithmetic on the SIMD
+  // (70B-shaped main kernel about 1 us faster over 7 same-box A/B rounds).
   while (h0) {
     if (!consume(b0)) return;
+    __builtin_amdgcn_s_setprio(2);
     h0 = load_next(b0);
+    __builtin_amdgcn_s_setprio(0);
     if (!h1) return;
     if (!consume(b1)) return;
+    __builtin_amdgcn_s_setprio(2);
     h1 = load_next(b1);
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
